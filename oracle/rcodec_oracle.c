@@ -1,0 +1,514 @@
+/*
+ * rcodec_oracle.c -- plain, slow CPU oracle of the inline-compression codec.
+ *
+ * TEST INFRASTRUCTURE ONLY (see rcodec_oracle.h).  Build with
+ *   gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * so that every float operation below is one correctly rounded IEEE binary32
+ * (or binary64) operation, with nothing fused.
+ *
+ * Style: every rounding decision is taken by an exact comparison written out
+ * in double precision, with a comment saying why the double arithmetic is
+ * exact.  Nothing here is blocked, fused or reordered for speed.
+ *
+ * Layout of one 2048-element tile (32-element blocks b = 0..63; element i of
+ * the tile lies in block i/32 at position e = i%32):
+ *
+ *   INT4 (1152 B):  nibble i of bytes [0,1024) (low nibble first) holds
+ *                   (sign << 3) | magnitude, magnitude 0..7;
+ *                   fp16 scale of block b at 1024 + 2b.
+ *   INT3 (896 B):   q2w plane = bytes [0,512): magnitude (2 bits) of element
+ *                   e of block b at bit 64b + 32*((e/2)%2) + 4*((e/2)/2) +
+ *                   2*(e%2); q1w plane = bytes [512,768): sign of tile element
+ *                   i at bit i; fp16 scale of block b at 768 + 2b.
+ *   FP8 (2304 B):   byte i = E4M3 code; fp32 scale of block b at 2048 + 4b.
+ *   MXFP4 (1088 B): nibble i of bytes [0,1024) = E2M1 code;
+ *                   E8M0 scale byte of block b at 1024 + b.
+ * All planes are little-endian bit streams (bit j of a plane is bit j%8 of
+ * its byte j/8).  Positions of the tail tile beyond n hold +0.
+ */
+#include "rcodec_oracle.h"
+
+#include <float.h>
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* sizes                                                               */
+/* ------------------------------------------------------------------ */
+
+static int codec_ok(rco_codec c)
+{
+    if (c.block != RCO_BLOCK_ELEMS) return 0;
+    switch (c.format) {
+    case RCO_FMT_INT4:     return c.scale == RCO_SCALE_FP16;
+    case RCO_FMT_INT3:     return c.scale == RCO_SCALE_FP16;
+    case RCO_FMT_FP8_E4M3: return c.scale == RCO_SCALE_FP32;
+    case RCO_FMT_MXFP4:    return c.scale == RCO_SCALE_E8M0;
+    default:               return 0;
+    }
+}
+
+/* Tile sizes: 1024 code bytes + 64 fp16 scales = 1152 B for INT4 and
+ * 512 + 256 code bytes + 128 = 896 B for INT3, the two sizes printed on
+ * "QuickReduce INT3 Quantization and Benchmarking on MI355" (Summary);
+ * FP8: 2048 code bytes + 64 fp32 scales; MXFP4: 1024 + 64 E8M0 bytes. */
+size_t rco_tile_bytes(rco_codec c)
+{
+    if (!codec_ok(c)) return 0;
+    switch (c.format) {
+    case RCO_FMT_INT4:     return 1152;
+    case RCO_FMT_INT3:     return 896;
+    case RCO_FMT_FP8_E4M3: return 2304;
+    case RCO_FMT_MXFP4:    return 1088;
+    }
+    return 0;
+}
+
+size_t rco_packed_bytes(rco_codec c, size_t n)
+{
+    return ((n + RCO_TILE_ELEMS - 1) / RCO_TILE_ELEMS) * rco_tile_bytes(c);
+}
+
+/* ------------------------------------------------------------------ */
+/* binary16 / bfloat16 conversions, written from the IEEE definitions  */
+/* ------------------------------------------------------------------ */
+
+float rco_bf16_to_f32(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return f;
+}
+
+float rco_f16_to_f32(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)       v = ldexp((double)m, -24);              /* subnormal */
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else              v = ldexp((double)(1024 + m), e - 25);
+    return (float)(s ? -v : v);                               /* exact */
+}
+
+/* Round |x| to a significand of p bits (p-1 stored) with exponent range
+ * [emin, emax], ties to even; returns the biased pattern without sign,
+ * or the infinity pattern on overflow.  a*2^(p-1-E) is an exact power-of-two
+ * scaling of a double, and nearbyint() rounds it to an integer with ties to
+ * even (default rounding mode), which is the definition of RNE. */
+static uint32_t round_to_format(double a, int p, int emin, int emax, int bias,
+                                uint32_t inf_pattern)
+{
+    int ex;
+    if (a == 0.0) return 0;
+    frexp(a, &ex);                 /* a = f*2^ex, f in [0.5,1) */
+    int E = ex - 1;                /* 2^E <= a < 2^(E+1)      */
+    if (E < emin) E = emin;        /* subnormal quantum 2^(emin-p+1) */
+    double q = nearbyint(ldexp(a, p - 1 - E));
+    double one = ldexp(1.0, p - 1);
+    if (q >= 2.0 * one) { q *= 0.5; E += 1; }   /* carried into next binade */
+    if (E > emax) return inf_pattern;
+    if (q < one) return (uint32_t)q;            /* subnormal (E == emin)   */
+    return ((uint32_t)(E + bias) << (p - 1)) | (uint32_t)(q - one);
+}
+
+uint16_t rco_f32_to_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x)) return sign | 0x7E00;
+    if (isinf(x)) return sign | 0x7C00;
+    return sign | (uint16_t)round_to_format(fabs((double)x), 11, -14, 15, 15, 0x7C00);
+}
+
+uint16_t rco_f32_to_bf16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x)) return sign | 0x7FC0;
+    if (isinf(x)) return sign | 0x7F80;
+    return sign | (uint16_t)round_to_format(fabs((double)x), 8, -126, 127, 127, 0x7F80);
+}
+
+/* ------------------------------------------------------------------ */
+/* narrow element formats                                              */
+/* ------------------------------------------------------------------ */
+
+/* OCP E4M3: bias 7, no infinities, the one NaN mantissa pattern is S.1111.111
+ * ("FP8 Formats for Deep Learning", abstract).  Largest finite = 448. */
+float rco_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else        v = ldexp((double)(8 + m), e - 10);
+    return (float)(s ? -v : v);
+}
+
+/* E2M1 (the MXFP4 element): 1 sign, 2 exponent (bias 1), 1 mantissa bit;
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN. */
+float rco_e2m1_decode(uint8_t n)
+{
+    int s = (n >> 3) & 1, e = (n >> 1) & 3, m = n & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (float)(s ? -v : v);
+}
+
+/* E8M0 shared scale (MX): value 2^(byte-127); 0xFF is NaN. */
+float rco_e8m0_decode(uint8_t b)
+{
+    if (b == 0xFF) return NAN;
+    return (float)ldexp(1.0, (int)b - 127);
+}
+
+/* Nearest entry of an increasing table of magnitudes val[0..cnt) to num/den
+ * (num >= 0, den > 0), ties to the even index, values beyond the last entry
+ * saturating to it.  Comparisons are exact: num and den are doubles holding
+ * binary32 values, every val[] and every midpoint of neighbours has at most
+ * 6 significant bits, so mid*den has at most 30 significant bits and is exact
+ * in binary64. */
+static int nearest_of_quotient(const double *val, int cnt, double num, double den)
+{
+    int lo = 0, hi = cnt - 1;                 /* largest c with val[c]*den <= num */
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (val[mid] * den <= num) lo = mid; else hi = mid - 1;
+    }
+    int c = lo;
+    if (c == cnt - 1) return c;               /* saturate */
+    double mid = 0.5 * (val[c] + val[c + 1]) * den;
+    if (num > mid) return c + 1;
+    if (num < mid) return c;
+    return (c % 2 == 0) ? c : c + 1;          /* tie: even code */
+}
+
+static double e4m3_mag[127];
+static double e2m1_mag[8];
+
+/* Filled once when the library is loaded, before any caller thread runs. */
+__attribute__((constructor)) static void init_tables(void)
+{
+    for (int c = 0; c < 127; ++c) e4m3_mag[c] = rco_e4m3_decode((uint8_t)c);
+    for (int c = 0; c < 8; ++c)   e2m1_mag[c] = rco_e2m1_decode((uint8_t)c);
+}
+
+/* E4M3 magnitude code of the exact quotient num/den, round to nearest even,
+ * saturating at 448 (code 0x7E). */
+int rco_e4m3_mag_of_quotient(double num, double den)
+{
+    return nearest_of_quotient(e4m3_mag, 127, num, den);
+}
+
+/* E2M1 magnitude code of an exact value, round to nearest even, saturating
+ * at 6 (code 7). */
+int rco_e2m1_mag_of(double y_abs)
+{
+    return nearest_of_quotient(e2m1_mag, 8, y_abs, 1.0);
+}
+
+/* Symmetric integer magnitude: the integer nearest to num/den, ties to even,
+ * clamped to qmax ("symmetric quantization", QuickReduce INT3 ... -- Method).
+ * num is |v| for a binary32 v, den an fp16 value.  Below the clamp k <= 7, so
+ * k*den and (k+1/2)*den = (2k+1)*den/2 have at most 15 significant bits and
+ * are exact in binary64; every comparison below is therefore exact. */
+int rco_int_mag_of_quotient(double num, double den, int qmax)
+{
+    if (num >= (qmax + 0.5) * den) return qmax;       /* RNE then clamp */
+    int k = (int)floor(num / den);                    /* candidate      */
+    while (k > 0 && k * den > num) --k;                /* make k*den <= num */
+    while ((k + 1) * den <= num) ++k;                  /* < (k+1)*den    */
+    double mid = (k + 0.5) * den;
+    int m;
+    if (num > mid)      m = k + 1;
+    else if (num < mid) m = k;
+    else                m = (k % 2 == 0) ? k : k + 1;
+    return m > qmax ? qmax : m;
+}
+
+/* ------------------------------------------------------------------ */
+/* block scale rules                                                   */
+/* ------------------------------------------------------------------ */
+
+/* FP16 block scale: the block absmax over qmax, one IEEE binary32 division,
+ * clamped to the largest half and rounded to fp16 (RNE; subnormal halves
+ * kept).  QuickReduce INT3 ... -- Method ("block-level FP16 scale"). */
+uint16_t rco_int_scale_bits(float amax, int qmax)
+{
+    float s32 = amax / (float)qmax;
+    if (s32 > 65504.0f) s32 = 65504.0f;
+    return rco_f32_to_f16(s32);
+}
+
+/* FP32 block scale for FP8: absmax/448 in binary32, so the block maximum maps
+ * to the largest E4M3 magnitude; scales below FLT_MIN are flushed to 0 and the
+ * block is then stored as zeros.  RCCLX ... -- Low-Precision Collectives
+ * (FP8 with computation in FP32). */
+float rco_fp8_scale(float amax)
+{
+    float s = amax / 448.0f;
+    return (s < FLT_MIN) ? 0.0f : s;
+}
+
+/* MX shared exponent: floor(log2(absmax)) minus the largest exponent of the
+ * element format (2 for E2M1), clamped to the E8M0 range; a zero block uses
+ * the smallest scale.  Microscaling Data Formats for Deep Learning (abstract:
+ * a per-block scale factor over narrow elements). */
+int rco_mx_exponent(float amax)
+{
+    int ex;
+    if (amax == 0.0f) return -127;
+    frexp((double)amax, &ex);            /* exact for binary32 subnormals too */
+    int e = (ex - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* ------------------------------------------------------------------ */
+/* bit planes                                                          */
+/* ------------------------------------------------------------------ */
+
+static void put_bits(uint8_t *plane, size_t pos, unsigned val, int width)
+{
+    for (int j = 0; j < width; ++j) {
+        size_t p = pos + (size_t)j;
+        if ((val >> j) & 1u) plane[p / 8] |= (uint8_t)(1u << (p % 8));
+        else                 plane[p / 8] &= (uint8_t)~(1u << (p % 8));
+    }
+}
+
+static unsigned get_bits(const uint8_t *plane, size_t pos, int width)
+{
+    unsigned v = 0;
+    for (int j = 0; j < width; ++j) {
+        size_t p = pos + (size_t)j;
+        v |= (unsigned)((plane[p / 8] >> (p % 8)) & 1u) << j;
+    }
+    return v;
+}
+
+/* Bit position, inside the q2w plane of a tile, of the 2-bit magnitude of
+ * element e of block b.  The block's 16 element pairs (2p, 2p+1) are dealt
+ * alternately to its two 32-bit words: pair p goes to word p%2, nibble p/2,
+ * the even element of the pair in the nibble's low two bits. */
+static size_t int3_q2w_pos(int b, int e)
+{
+    int p = e / 2;
+    return (size_t)64 * b + 32 * (p % 2) + 4 * (p / 2) + 2 * (e % 2);
+}
+
+static void put_u16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+static uint16_t get_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static void put_f32(uint8_t *p, float f) { memcpy(p, &f, 4); }
+static float get_f32(const uint8_t *p) { float f; memcpy(&f, p, 4); return f; }
+
+/* ------------------------------------------------------------------ */
+/* tile encode / decode                                                */
+/* ------------------------------------------------------------------ */
+
+static float widen(int dt, const void *in, size_t i)
+{
+    if (dt == RCO_DT_FP32) return ((const float *)in)[i];
+    if (dt == RCO_DT_FP16) return rco_f16_to_f32(((const uint16_t *)in)[i]);
+    return rco_bf16_to_f32(((const uint16_t *)in)[i]);
+}
+
+static float block_absmax(const float *v)
+{
+    float a = 0.0f;
+    for (int e = 0; e < RCO_BLOCK_ELEMS; ++e) {
+        float m = fabsf(v[e]);
+        if (m > a) a = m;
+    }
+    return a;
+}
+
+/* Encode the 2048 binary32 values v[] of one tile into dst (tile bytes). */
+static void encode_tile(rco_codec c, const float *v, uint8_t *dst)
+{
+    size_t tb = rco_tile_bytes(c);
+    memset(dst, 0, tb);
+    for (int b = 0; b < 64; ++b) {
+        const float *vb = v + 32 * b;
+        float amax = block_absmax(vb);
+        if (c.format == RCO_FMT_INT4 || c.format == RCO_FMT_INT3) {
+            int qmax = (c.format == RCO_FMT_INT4) ? 7 : 3;
+            uint16_t h = rco_int_scale_bits(amax, qmax);
+            float s = rco_f16_to_f32(h);
+            if (s == 0.0f) continue;                 /* zero block: all bytes 0 */
+            put_u16(dst + (c.format == RCO_FMT_INT4 ? 1024 : 768) + 2 * b, h);
+            for (int e = 0; e < 32; ++e) {
+                unsigned sign = signbit(vb[e]) ? 1u : 0u;
+                unsigned mag = (unsigned)rco_int_mag_of_quotient(fabs((double)vb[e]), s, qmax);
+                size_t i = (size_t)32 * b + e;
+                if (c.format == RCO_FMT_INT4) {
+                    put_bits(dst, 4 * i, (sign << 3) | mag, 4);
+                } else {
+                    put_bits(dst, int3_q2w_pos(b, e), mag, 2);
+                    put_bits(dst + 512, i, sign, 1);
+                }
+            }
+        } else if (c.format == RCO_FMT_FP8_E4M3) {
+            float s = rco_fp8_scale(amax);
+            if (s == 0.0f) continue;
+            put_f32(dst + 2048 + 4 * b, s);
+            for (int e = 0; e < 32; ++e) {
+                unsigned sign = signbit(vb[e]) ? 1u : 0u;
+                unsigned mag = (unsigned)rco_e4m3_mag_of_quotient(fabs((double)vb[e]), s);
+                dst[32 * b + e] = (uint8_t)((sign << 7) | mag);
+            }
+        } else { /* MXFP4 */
+            int ex = rco_mx_exponent(amax);
+            dst[1024 + b] = (uint8_t)(ex + 127);
+            for (int e = 0; e < 32; ++e) {
+                unsigned sign = signbit(vb[e]) ? 1u : 0u;
+                double y = ldexp(fabs((double)vb[e]), -ex);        /* exact */
+                unsigned mag = (unsigned)rco_e2m1_mag_of(y);
+                put_bits(dst, 4 * ((size_t)32 * b + e), (sign << 3) | mag, 4);
+            }
+        }
+    }
+}
+
+/* Decode element i (0..2047) of one tile to binary32.  INT and MX products
+ * are exact; the FP8 product is one binary32 multiplication. */
+static float decode_elem(rco_codec c, const uint8_t *src, int i)
+{
+    int b = i / 32, e = i % 32;
+    switch (c.format) {
+    case RCO_FMT_INT4: {
+        unsigned nib = get_bits(src, 4 * (size_t)i, 4);
+        float s = rco_f16_to_f32(get_u16(src + 1024 + 2 * b));
+        float d = (float)((double)(nib & 7u) * s);
+        return (nib & 8u) ? -d : d;
+    }
+    case RCO_FMT_INT3: {
+        unsigned mag = get_bits(src, int3_q2w_pos(b, e), 2);
+        unsigned sign = get_bits(src + 512, (size_t)i, 1);
+        float s = rco_f16_to_f32(get_u16(src + 768 + 2 * b));
+        float d = (float)((double)mag * s);
+        return sign ? -d : d;
+    }
+    case RCO_FMT_FP8_E4M3: {
+        float dec = rco_e4m3_decode(src[i]);
+        float s = get_f32(src + 2048 + 4 * b);
+        return dec * s;                                   /* RN32 */
+    }
+    default: { /* MXFP4 */
+        float dec = rco_e2m1_decode((uint8_t)get_bits(src, 4 * (size_t)i, 4));
+        uint8_t sb = src[1024 + b];
+        if (sb == 0xFF) return NAN;
+        return (float)ldexp((double)dec, (int)sb - 127);  /* exact */
+    }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* public operations                                                   */
+/* ------------------------------------------------------------------ */
+
+static int dtype_ok(int dt)
+{
+    return dt == RCO_DT_FP32 || dt == RCO_DT_FP16 || dt == RCO_DT_BF16;
+}
+
+int rco_quantize_pack_tiles(rco_codec c, int in_dtype, const void *in, size_t n,
+                            void *out, size_t t0, size_t t1)
+{
+    if (!codec_ok(c) || !dtype_ok(in_dtype)) return RCO_ERR_UNSUPPORTED;
+    if (n == 0) return RCO_OK;
+    if (!in || !out) return RCO_ERR_NULL;
+    size_t tb = rco_tile_bytes(c);
+    float v[RCO_TILE_ELEMS];
+    for (size_t t = t0; t < t1; ++t) {
+        for (int j = 0; j < RCO_TILE_ELEMS; ++j) {
+            size_t i = t * RCO_TILE_ELEMS + (size_t)j;
+            v[j] = (i < n) ? widen(in_dtype, in, i) : 0.0f;
+        }
+        encode_tile(c, v, (uint8_t *)out + t * tb);
+    }
+    return RCO_OK;
+}
+
+int rco_quantize_pack(rco_codec c, int in_dtype, const void *in, size_t n, void *out)
+{
+    size_t tiles = (n + RCO_TILE_ELEMS - 1) / RCO_TILE_ELEMS;
+    return rco_quantize_pack_tiles(c, in_dtype, in, n, out, 0, tiles);
+}
+
+int rco_unpack_dequant(rco_codec c, const void *in, size_t n, int out_dtype, void *out)
+{
+    if (!codec_ok(c) || !dtype_ok(out_dtype)) return RCO_ERR_UNSUPPORTED;
+    if (n == 0) return RCO_OK;
+    if (!in || !out) return RCO_ERR_NULL;
+    size_t tb = rco_tile_bytes(c);
+    for (size_t i = 0; i < n; ++i) {
+        const uint8_t *tile = (const uint8_t *)in + (i / RCO_TILE_ELEMS) * tb;
+        float d = decode_elem(c, tile, (int)(i % RCO_TILE_ELEMS));
+        if (out_dtype == RCO_DT_FP32)      ((float *)out)[i] = d;
+        else if (out_dtype == RCO_DT_FP16) ((uint16_t *)out)[i] = rco_f32_to_f16(d);
+        else                               ((uint16_t *)out)[i] = rco_f32_to_bf16(d);
+    }
+    return RCO_OK;
+}
+
+/* acc = d_0, then acc = RN32(acc + d_k) for k = 1..K-1 in stream order
+ * (RCCLX ... -- Low-Precision Collectives: computation stays in FP32), then
+ * the sums are requantized with the same codec.  Positions beyond n are +0
+ * whatever the input codes there say. */
+int rco_dequant_reduce_requant_tiles(rco_codec c, const void *const *ins, int k,
+                                     size_t n, void *out, float *sum_out,
+                                     size_t t0, size_t t1)
+{
+    if (!codec_ok(c)) return RCO_ERR_UNSUPPORTED;
+    if (k < 1 || k > RCO_MAX_STREAMS) return RCO_ERR_RANGE;
+    if (n == 0) return RCO_OK;
+    if (!ins || !out) return RCO_ERR_NULL;
+    for (int s = 0; s < k; ++s) if (!ins[s]) return RCO_ERR_NULL;
+    size_t tb = rco_tile_bytes(c);
+    float acc[RCO_TILE_ELEMS];
+    for (size_t t = t0; t < t1; ++t) {
+        for (int j = 0; j < RCO_TILE_ELEMS; ++j) {
+            size_t i = t * RCO_TILE_ELEMS + (size_t)j;
+            if (i >= n) { acc[j] = 0.0f; continue; }
+            float a = decode_elem(c, (const uint8_t *)ins[0] + t * tb, j);
+            for (int s = 1; s < k; ++s)
+                a = a + decode_elem(c, (const uint8_t *)ins[s] + t * tb, j);
+            acc[j] = a;
+            if (sum_out) sum_out[i] = a;
+        }
+        encode_tile(c, acc, (uint8_t *)out + t * tb);
+    }
+    return RCO_OK;
+}
+
+int rco_dequant_reduce_requant(rco_codec c, const void *const *ins, int k, size_t n,
+                               void *out, float *sum_out)
+{
+    size_t tiles = (n + RCO_TILE_ELEMS - 1) / RCO_TILE_ELEMS;
+    return rco_dequant_reduce_requant_tiles(c, ins, k, n, out, sum_out, 0, tiles);
+}
+
+/* ------------------------------------------------------------------ */
+/* element-wise loops (pins)                                           */
+/* ------------------------------------------------------------------ */
+
+void rco_map_f32_to_f16(const float *x, uint16_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_f32_to_f16(x[i]); }
+void rco_map_f32_to_bf16(const float *x, uint16_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_f32_to_bf16(x[i]); }
+void rco_map_f16_to_f32(const uint16_t *x, float *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_f16_to_f32(x[i]); }
+void rco_map_bf16_to_f32(const uint16_t *x, float *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_bf16_to_f32(x[i]); }
+void rco_map_e4m3_mag(const double *num, const double *den, int32_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_e4m3_mag_of_quotient(num[i], den[i]); }
+void rco_map_e2m1_mag(const double *v, int32_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_e2m1_mag_of(v[i]); }
+void rco_map_int_mag(const double *num, const double *den, int qmax, int32_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_int_mag_of_quotient(num[i], den[i], qmax); }
+void rco_map_int_scale_bits(const float *amax, int qmax, uint16_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_int_scale_bits(amax[i], qmax); }
+void rco_map_fp8_scale(const float *amax, float *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_fp8_scale(amax[i]); }
+void rco_map_mx_exponent(const float *amax, int32_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_mx_exponent(amax[i]); }

@@ -1,0 +1,105 @@
+/*
+ * rcodec_oracle.h -- plain CPU oracle of the inline-compression codec.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this code: only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no source with the HIP library.
+ *
+ * What it computes (the spec of record, one definition per step):
+ *   - block quantization with one scale per 32-element block, symmetric
+ *     integer codes and an FP16 block scale, the 3-bit codes split into a
+ *     low-2-bit plane (q2w) and a high-bit plane (q1w)
+ *       [QuickReduce INT3 Quantization and Benchmarking on MI355 -- Method];
+ *   - fixed 2048-element tiles that pack to 1152 B (INT4) and 896 B (INT3)
+ *       [same page -- Summary];
+ *   - FP8 E4M3 codes with an FP32 block scale, FP32 accumulation of the
+ *     dequantized streams
+ *       [RCCLX: Innovating GPU communications on AMD platforms --
+ *        Low-Precision Collectives];
+ *   - E4M3 with no infinities and a single NaN mantissa pattern
+ *       [FP8 Formats for Deep Learning -- abstract];
+ *   - MX blocks: a shared power-of-two scale over narrow elements, and the
+ *     MXFP4 direct cast
+ *       [Microscaling Data Formats for Deep Learning -- abstract;
+ *        ML-SpecQD: Multi-Level Speculative Decoding with Quantized Drafts].
+ * Every step the pages leave open is fixed once here and listed as a
+ * "reading" in the design notes of the repository.
+ *
+ * All functions take host pointers, run synchronously on one thread and
+ * allocate nothing.  Status codes are numerically identical to the GPU
+ * library's; a test checks that they agree.
+ */
+#ifndef RCODEC_ORACLE_H
+#define RCODEC_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RCO_TILE_ELEMS 2048
+#define RCO_BLOCK_ELEMS 32
+#define RCO_MAX_STREAMS 16
+
+enum { RCO_FMT_INT4 = 1, RCO_FMT_INT3 = 2, RCO_FMT_FP8_E4M3 = 3, RCO_FMT_MXFP4 = 4 };
+enum { RCO_SCALE_FP16 = 1, RCO_SCALE_FP32 = 2, RCO_SCALE_E8M0 = 3 };
+enum { RCO_DT_FP32 = 1, RCO_DT_FP16 = 2, RCO_DT_BF16 = 3 };
+enum { RCO_OK = 0, RCO_ERR_NULL = 1, RCO_ERR_UNSUPPORTED = 2, RCO_ERR_ALIGN = 3,
+       RCO_ERR_RANGE = 4, RCO_ERR_HIP = 5 };
+
+typedef struct { int32_t format, scale, block; } rco_codec;
+
+/* ---- sizes ---------------------------------------------------------- */
+size_t rco_tile_bytes(rco_codec c);               /* 0 when unsupported   */
+size_t rco_packed_bytes(rco_codec c, size_t n);   /* ceil(n/2048) * tile  */
+
+/* ---- whole-stream operations (host buffers) ------------------------- */
+int rco_quantize_pack(rco_codec c, int in_dtype, const void *in, size_t n, void *out);
+int rco_unpack_dequant(rco_codec c, const void *in, size_t n, int out_dtype, void *out);
+int rco_dequant_reduce_requant(rco_codec c, const void *const *ins, int k, size_t n,
+                               void *out, float *sum_out);
+/* Same as above, restricted to tiles [t0, t1): used to time the oracle on a
+ * bounded sample and to compute sampled outputs of very large streams.
+ * Pointers address the whole stream; only the listed tiles are touched.  */
+int rco_quantize_pack_tiles(rco_codec c, int in_dtype, const void *in, size_t n,
+                            void *out, size_t t0, size_t t1);
+int rco_dequant_reduce_requant_tiles(rco_codec c, const void *const *ins, int k,
+                                     size_t n, void *out, float *sum_out,
+                                     size_t t0, size_t t1);
+
+/* ---- scalar building blocks, exported so the pins can test them ------ */
+float    rco_bf16_to_f32(uint16_t h);
+uint16_t rco_f32_to_bf16(float x);                /* RNE, IEEE overflow  */
+float    rco_f16_to_f32(uint16_t h);
+uint16_t rco_f32_to_f16(float x);                 /* RNE, IEEE overflow  */
+float    rco_e4m3_decode(uint8_t code);           /* OCP E4M3 ("FN")     */
+float    rco_e2m1_decode(uint8_t nibble);
+float    rco_e8m0_decode(uint8_t byte);           /* 2^(byte-127), 0xFF NaN */
+/* magnitude code of |num|/den rounded to nearest, ties to even code,
+ * saturating; num, den exact doubles, den > 0 */
+int      rco_e4m3_mag_of_quotient(double num, double den);   /* 0..126 */
+int      rco_e2m1_mag_of(double y_abs);                      /* 0..7   */
+int      rco_int_mag_of_quotient(double num, double den, int qmax);
+/* per-block scale rules; amax >= 0 */
+uint16_t rco_int_scale_bits(float amax, int qmax);   /* fp16 bits       */
+float    rco_fp8_scale(float amax);                  /* 0 when flushed  */
+int      rco_mx_exponent(float amax);                /* -127..127       */
+
+/* element-wise loops over the scalar rules above (for the pins) */
+void rco_map_f32_to_f16(const float *x, uint16_t *y, size_t n);
+void rco_map_f32_to_bf16(const float *x, uint16_t *y, size_t n);
+void rco_map_f16_to_f32(const uint16_t *x, float *y, size_t n);
+void rco_map_bf16_to_f32(const uint16_t *x, float *y, size_t n);
+void rco_map_e4m3_mag(const double *num, const double *den, int32_t *y, size_t n);
+void rco_map_e2m1_mag(const double *v, int32_t *y, size_t n);
+void rco_map_int_mag(const double *num, const double *den, int qmax, int32_t *y, size_t n);
+void rco_map_int_scale_bits(const float *amax, int qmax, uint16_t *y, size_t n);
+void rco_map_fp8_scale(const float *amax, float *y, size_t n);
+void rco_map_mx_exponent(const float *amax, int32_t *y, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,208 @@
+"""Brute-force statement of the codec, independent of the oracle's code.
+
+Used only to pin the oracle on small inputs.  Every rounding decision is an
+argmin over all candidate codes with exact rational arithmetic
+(``fractions.Fraction``); binary32 / binary16 arithmetic goes through numpy
+scalars (IEEE), the E4M3 value table through torch's ``float8_e4m3fn``.  Tile
+layouts are written at the 32-bit-word level, the INT3 planes as bit-plane
+splits of per-group nibble words, which is a different description from the
+oracle's per-element bit positions.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+TILE, BLOCK = 2048, 32
+
+
+def _e4m3_table():
+    import torch
+    vals = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    return [Fraction(float(v)) for v in vals]
+
+
+E4M3 = _e4m3_table()
+E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+        Fraction(4), Fraction(6)]
+
+
+def nearest_code(q: Fraction, table) -> int:
+    """argmin_c |q - table[c]|, ties to the even code (table increasing)."""
+    best, bestd = 0, abs(q - table[0])
+    for c in range(1, len(table)):
+        d = abs(q - table[c])
+        if d < bestd or (d == bestd and c % 2 == 0):
+            best, bestd = c, d
+    return best
+
+
+def int_mag(v: float, s: float, qmax: int) -> int:
+    q = Fraction(abs(float(v))) / Fraction(float(s))
+    return nearest_code(q, [Fraction(k) for k in range(qmax + 1)])
+
+
+def int_scale(a: np.float32, qmax: int) -> np.float16:
+    s32 = np.float32(a) / np.float32(qmax)
+    if s32 > np.float32(65504.0):
+        s32 = np.float32(65504.0)
+    return np.float16(s32)
+
+
+def fp8_scale(a: np.float32) -> np.float32:
+    s = np.float32(a) / np.float32(448.0)
+    return np.float32(0.0) if s < np.finfo(np.float32).tiny else s
+
+
+def mx_exponent(a: float) -> int:
+    if a == 0:
+        return -127
+    fa = Fraction(float(a))
+    e = -160
+    while Fraction(2) ** (e + 1) <= fa:
+        e += 1
+    return max(-127, min(127, e - 2))
+
+
+def _sign(v) -> int:
+    return 1 if np.signbit(np.float32(v)) else 0
+
+
+def _words_to_bytes(words) -> bytes:
+    return b"".join(int(w & 0xFFFFFFFF).to_bytes(4, "little") for w in words)
+
+
+def encode_tile(fmt: str, v: np.ndarray) -> bytes:
+    """v: 2048 float32 values (tail already zero)."""
+    v = np.asarray(v, dtype=np.float32)
+    assert v.size == TILE
+    codes = bytearray()
+    scales = bytearray()
+    int3_q2w, int3_q1w = [], []
+    for b in range(64):
+        vb = v[32 * b:32 * b + 32]
+        a = np.max(np.abs(vb))
+        if fmt in ("int4", "int3"):
+            qmax = 7 if fmt == "int4" else 3
+            h = int_scale(a, qmax)
+            s = float(h)
+            if s == 0.0:
+                nib = [0] * 32
+                hbits = 0
+            else:
+                nib = [(_sign(x) << 3) | int_mag(x, s, qmax) for x in vb]
+                hbits = int(h.view(np.uint16))
+            scales += hbits.to_bytes(2, "little")
+            if fmt == "int4":
+                words = [sum(nib[8 * d + j] << (4 * j) for j in range(8)) for d in range(4)]
+                codes += _words_to_bytes(words)
+            else:
+                # group g = elements 4j+g, nibble j of word N_g
+                N = [sum(nib[4 * j + g] << (4 * j) for j in range(8)) for g in range(4)]
+                m = 0x33333333
+                w0 = (N[0] & m) | ((N[1] & m) << 2)
+                w1 = (N[2] & m) | ((N[3] & m) << 2)
+                hw = ((N[0] >> 3) & 0x11111111) | ((N[1] >> 2) & 0x22222222) | \
+                     ((N[2] >> 1) & 0x44444444) | (N[3] & 0x88888888)
+                int3_q2w += [w0, w1]
+                int3_q1w += [hw]
+        elif fmt == "fp8":
+            s = fp8_scale(a)
+            if s == 0:
+                codes += bytes(32)
+            else:
+                for x in vb:
+                    q = Fraction(abs(float(x))) / Fraction(float(s))
+                    codes.append((_sign(x) << 7) | nearest_code(q, E4M3))
+            scales += np.float32(s).tobytes()
+        elif fmt == "mxfp4":
+            e = mx_exponent(float(a))
+            nib = []
+            for x in vb:
+                y = Fraction(abs(float(x))) * Fraction(2) ** (-e)
+                nib.append((_sign(x) << 3) | nearest_code(y, E2M1))
+            words = [sum(nib[8 * d + j] << (4 * j) for j in range(8)) for d in range(4)]
+            codes += _words_to_bytes(words)
+            scales.append(e + 127)
+        else:
+            raise ValueError(fmt)
+    if fmt == "int3":
+        return _words_to_bytes(int3_q2w) + _words_to_bytes(int3_q1w) + bytes(scales)
+    return bytes(codes) + bytes(scales)
+
+
+def encode(fmt: str, x_f32: np.ndarray) -> bytes:
+    x = np.asarray(x_f32, dtype=np.float32)
+    tiles = (x.size + TILE - 1) // TILE
+    out = b""
+    for t in range(tiles):
+        v = np.zeros(TILE, dtype=np.float32)
+        chunk = x[t * TILE:(t + 1) * TILE]
+        v[:chunk.size] = chunk
+        out += encode_tile(fmt, v)
+    return out
+
+
+def decode_tile(fmt: str, tile: bytes) -> np.ndarray:
+    """Exact decode of one tile to float32 values."""
+    out = np.zeros(TILE, dtype=np.float32)
+    words = lambda off, cnt: [int.from_bytes(tile[off + 4 * i: off + 4 * i + 4], "little")
+                              for i in range(cnt)]
+    for b in range(64):
+        if fmt in ("int4", "int3"):
+            soff = 1024 if fmt == "int4" else 768
+            s = float(np.frombuffer(tile[soff + 2 * b: soff + 2 * b + 2], dtype=np.float16)[0])
+            if fmt == "int4":
+                ws = words(16 * b, 4)
+                nib = [(ws[e // 8] >> (4 * (e % 8))) & 15 for e in range(32)]
+            else:
+                w0, w1 = words(8 * b, 2)
+                (hw,) = words(512 + 4 * b, 1)
+                nib = [0] * 32
+                for g in range(4):
+                    W = w0 if g < 2 else w1
+                    Ng = ((W >> (2 * (g & 1))) & 0x33333333) | ((hw << (3 - g)) & 0x88888888)
+                    for j in range(8):
+                        nib[4 * j + g] = (Ng >> (4 * j)) & 15
+            for e in range(32):
+                mag = nib[e] & 7
+                val = np.float32(float(Fraction(mag) * Fraction(s)))
+                out[32 * b + e] = -val if nib[e] & 8 else val
+        elif fmt == "fp8":
+            s = np.frombuffer(tile[2048 + 4 * b: 2052 + 4 * b], dtype=np.float32)[0]
+            for e in range(32):
+                c = tile[32 * b + e]
+                dec = np.float32(float(E4M3[c & 127])) if (c & 127) != 127 else np.float32(np.nan)
+                val = dec * s                      # one binary32 product (IEEE)
+                out[32 * b + e] = -val if c & 128 else val
+        else:
+            ws = words(16 * b, 4)
+            e8 = tile[1024 + b]
+            for e in range(32):
+                nb = (ws[e // 8] >> (4 * (e % 8))) & 15
+                val = np.float32(float(E2M1[nb & 7] * Fraction(2) ** (e8 - 127)))
+                out[32 * b + e] = -val if nb & 8 else val
+    return out
+
+
+def tile_bytes(fmt: str) -> int:
+    return {"int4": 1152, "int3": 896, "fp8": 2304, "mxfp4": 1088}[fmt]
+
+
+def reduce(fmt: str, streams, n: int):
+    """Decode every stream, add in stream order in binary32, requantize."""
+    tb = tile_bytes(fmt)
+    tiles = (n + TILE - 1) // TILE
+    out = b""
+    sums = np.zeros(n, dtype=np.float32)
+    for t in range(tiles):
+        acc = None
+        for s in streams:
+            d = decode_tile(fmt, bytes(s[t * tb:(t + 1) * tb]))
+            acc = d.copy() if acc is None else (acc + d).astype(np.float32)
+        lim = min(TILE, n - t * TILE)
+        acc[lim:] = 0.0
+        sums[t * TILE:t * TILE + lim] = acc[:lim]
+        out += encode_tile(fmt, acc)
+    return out, sums
