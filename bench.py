@@ -1,0 +1,272 @@
+"""Benchmark of the codec hot path on one MI355X.
+
+One step = one pass of the whole hot path over one message: INT3
+quantize_pack of a 64 MiB bf16 message (33,554,432 Student-t values) into the
+first of four packed stream buffers, then a 4-stream dequant_reduce_requant of
+that stream and three pre-packed peer streams into one packed output.  Inputs
+are resident in HBM before timing starts; eight buffer sets are rotated so the
+working set (about 1 GiB) defeats the 256 MiB Infinity Cache.
+
+Prints one JSON line: value = uncompressed GB/s (input bytes of the quantize
+plus K x message bytes of the reduce, per second), a `roofline` object for the
+dominant kernel (algorithmic bytes per launch / average launch time from HIP
+events, against 8 TB/s) and a `cpu_baseline` object (the plain C oracle on
+the host cores over the same workload).
+
+Extra modes:
+  --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc` runs of this
+                                        script into profiles/traffic_*.json
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "codec GB/s (uncompressed bytes) and % of HBM peak, 64 MB INT3 quant+reduce"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_int3_64MiB.json")
+KERNEL_SOURCES = ["reduction_codec_amd/csrc/rc_device.hpp", "reduction_codec_amd/csrc/rc_kernels.hip"]
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mib", type=int, default=64, help="message size in MiB of bf16")
+    ap.add_argument("--k", type=int, default=4, help="streams in the reduce")
+    ap.add_argument("--fmt", default="int3", choices=["int3", "int4", "fp8", "mxfp4"])
+    ap.add_argument("--sets", type=int, default=0, help="rotation buffer sets (0 = enough for 1 GiB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- PMC ----
+
+def _read_counter_rows(d: str):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
+        import csv
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by
+    what the same counters read for the plain copy kernel of known size."""
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _read_counter_rows(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def find(table, key):
+        hits = [v for k, v in table.items() if key in k]
+        return hits[0] if hits else None
+
+    copy_f, copy_w = find(fetch, "copy_kernel"), find(write, "copy_kernel")
+    fscale = COPY_BYTES / (copy_f * 1024.0) if copy_f else None
+    wscale = COPY_BYTES / (copy_w * 1024.0) if copy_w else None
+    out = {"kernel_source_sha": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "fetch_scale": fscale, "write_scale": wscale,
+           "kernels": {}}
+    for key in ("reduce_kernel", "quantize_kernel"):
+        f, w = find(fetch, key), find(write, key)
+        if f is None or w is None or fscale is None or wscale is None:
+            continue
+        out["kernels"][key] = {"fetch_kib": f, "write_kib": w,
+                               "bytes": f * 1024.0 * fscale + w * 1024.0 * wscale}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def traffic_for(kernel_key: str):
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel_key)
+    return k["bytes"] if k else None
+
+
+# -------------------------------------------------------------- bench ----
+
+def main():
+    args = parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return 0
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only: this codec build has no multi-GPU path "
+                         "(run with --gpus 1)\n")
+        return 2
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import reduction_codec_amd as rca
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    codec = rca.CODECS[args.fmt]
+    n = args.mib * (1 << 20) // 2
+    K = args.k
+    pb = rca.packed_bytes(codec, n)
+    tiles = -(-n // 2048)
+    set_bytes = 2 * n + (K + 1) * pb
+    sets = args.sets or max(2, -(-(1 << 30) // set_bytes))
+
+    # seeded inputs: message k = Student-t nu=4 bf16, seed 500+k
+    host = [datagen.bf16_student4(2 * n, k) for k in range(K)]
+    dev_msgs = [torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev) for h in host]
+    peers = [rca.quantize_pack(m, codec) for m in dev_msgs]           # what the peers would send
+    bufs = []
+    for s in range(sets):
+        x = dev_msgs[0].clone()
+        streams = [torch.empty(pb, dtype=torch.uint8, device=dev)] + [p.clone() for p in peers[1:]]
+        out = torch.empty(pb, dtype=torch.uint8, device=dev)
+        bufs.append((x, streams, out))
+    torch.cuda.synchronize()
+
+    def step(i):
+        x, streams, out = bufs[i % sets]
+        rca.quantize_pack(x, codec, out=streams[0])
+        rca.dequant_reduce_requant(streams, codec, n, out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel launch durations (HIP events on the launch stream)
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    def q_only(i):
+        x, streams, _ = bufs[i % sets]
+        rca.quantize_pack(x, codec, out=streams[0])
+
+    def r_only(i):
+        _, streams, out = bufs[i % sets]
+        rca.dequant_reduce_requant(streams, codec, n, out=out)
+
+    reps = max(20, args.steps)
+    tq = timed(q_only, reps)
+    tr = timed(r_only, reps)
+    q_ms, r_ms = sum(tq) / len(tq), sum(tr) / len(tr)
+
+    # plain copy of 256 MiB: the achievable-bandwidth reference in this run
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    tc = timed(lambda i: rca.copy(dst, src), 20)
+    c_ms = sum(tc) / len(tc)
+    del src, dst
+
+    q_bytes = 2 * n + pb                      # algorithmic HBM bytes of one quantize launch
+    r_bytes = (K + 1) * pb                    # K packed streams in, one packed stream out
+    unc = 2 * n + K * 2 * n                   # uncompressed bytes processed per step
+    value = unc / (ms * 1e-3) / 1e9
+    step_hbm = (q_bytes + r_bytes) / (ms * 1e-3) / 1e9
+    dom_key, dom_bytes, dom_ms = ("reduce_kernel", r_bytes, r_ms) if r_ms >= q_ms else \
+        ("quantize_kernel", q_bytes, q_ms)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_key),
+            "kernel": f"{dom_key}<{args.fmt}" + (f", K={K}>" if dom_key == "reduce_kernel" else ", bf16>"),
+            "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args, host, n, K)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.mib} MiB bf16 Student-t(nu=4) message: {args.fmt.upper()} quantize_pack + "
+                               f"{K}-stream dequant_reduce_requant", "format": args.fmt, "n": n, "k": K,
+                   "tiles": tiles, "rotation_sets": sets, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "breakdown": {
+            "quantize_ms": round(q_ms, 5), "quantize_hbm_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "quantize_uncompressed_gbs": round(2 * n / (q_ms * 1e-3) / 1e9, 1),
+            "reduce_ms": round(r_ms, 5), "reduce_hbm_gbs": round(r_bytes / (r_ms * 1e-3) / 1e9, 1),
+            "reduce_uncompressed_gbs": round(K * 2 * n / (r_ms * 1e-3) / 1e9, 1),
+            "step_hbm_gbs": round(step_hbm, 1), "step_hbm_frac": round(step_hbm / HBM_PEAK_GBS, 4),
+            "copy_256MiB_gbs": round(2 * COPY_BYTES / (c_ms * 1e-3) / 1e9, 1),
+            "host_wall_ms_per_step": round(wall_ms, 5),
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(args, host, n, K):
+    """The oracle as it stands, over the same workload on the host cores:
+    quantize the message, then reduce it with the peers (packed by the oracle,
+    untimed), tile ranges split over all host threads."""
+    import oracle
+    c = oracle.CODECS[args.fmt]
+    threads = max(1, len(os.sched_getaffinity(0)))
+    tiles = -(-n // 2048)
+    # bounded sample: the first tiles of the message, sized to ~10-30 s of CPU time
+    per_elem_s = {"int3": 1.4e-7, "int4": 1.6e-7, "fp8": 3e-7, "mxfp4": 1.2e-7}[args.fmt] * (K / 4 + 0.3)
+    sample_tiles = min(tiles, max(256, int(15.0 / (per_elem_s * 2048))))
+    ns = sample_tiles * 2048
+    msgs = [h[:ns] for h in host]
+    peers = [oracle.quantize_pack_parallel(c, m, dtype=oracle.DT_BF16, threads=threads) for m in msgs]
+    t0 = time.perf_counter()
+    p0 = oracle.quantize_pack_parallel(c, msgs[0], dtype=oracle.DT_BF16, threads=threads)
+    oracle.dequant_reduce_requant_parallel(c, [p0] + peers[1:], ns, threads=threads)
+    dt = time.perf_counter() - t0
+    unc = 2 * ns + K * 2 * ns
+    return {"value": round(unc / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_tiles} tiles ({ns} elements) of the same message and peers; "
+                      f"quantize + {K}-stream reduce, tile ranges over {threads} threads, {dt:.2f} s wall"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

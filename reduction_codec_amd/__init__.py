@@ -1,0 +1,197 @@
+"""Python binding of the MI355X codec library ``librcodec.so``.
+
+Argument marshalling only: every step of the codec runs in the HIP kernels
+behind the C ABI declared in ``include/rcodec.h``.  PyTorch provides device
+memory and the current stream; nothing here computes on the CPU, and there is
+no fallback: if the library is not built, every call raises.
+
+Entry points (same names as the C ABI, minus the ``rc_`` prefix):
+
+* ``quantize_pack(x, codec)``             -> packed uint8 tensor
+* ``unpack_dequant(packed, codec, n, dtype)`` -> tensor of n values
+* ``dequant_reduce_requant(streams, codec, n, sum_out=False)``
+                                           -> (packed, fp32 sums or None)
+* ``tile_bytes(codec)``, ``packed_bytes(codec, n)``, ``copy(dst, src)``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # must load before librcodec.so: both share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librcodec.so")
+
+TILE = 2048
+BLOCK = 32
+MAX_STREAMS = 16
+
+FMT_INT4, FMT_INT3, FMT_FP8_E4M3, FMT_MXFP4 = 1, 2, 3, 4
+SCALE_FP16, SCALE_FP32, SCALE_E8M0 = 1, 2, 3
+DT_FP32, DT_FP16, DT_BF16 = 1, 2, 3
+OK, ERR_NULL, ERR_UNSUPPORTED, ERR_ALIGN, ERR_RANGE, ERR_HIP = 0, 1, 2, 3, 4, 5
+
+
+class Codec(ctypes.Structure):
+    """rc_codec: element format, scale type, block size (passed by value)."""
+    _fields_ = [("format", ctypes.c_int32), ("scale", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"Codec({self.format}, {self.scale}, {self.block})"
+
+
+INT4 = Codec(FMT_INT4, SCALE_FP16, BLOCK)
+INT3 = Codec(FMT_INT3, SCALE_FP16, BLOCK)
+FP8 = Codec(FMT_FP8_E4M3, SCALE_FP32, BLOCK)
+MXFP4 = Codec(FMT_MXFP4, SCALE_E8M0, BLOCK)
+CODECS = {"int4": INT4, "int3": INT3, "fp8": FP8, "mxfp4": MXFP4}
+
+_DTYPES = {torch.float32: DT_FP32, torch.float16: DT_FP16, torch.bfloat16: DT_BF16}
+_lib = None
+
+
+class CodecError(RuntimeError):
+    """A non-zero rc_status from the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().rc_status_str(status).decode()} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librcodec.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                           "(the codec has no CPU fallback)")
+    l = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    l.rc_tile_bytes.restype, l.rc_tile_bytes.argtypes = sz, [Codec]
+    l.rc_packed_bytes.restype, l.rc_packed_bytes.argtypes = sz, [Codec, sz]
+    l.rc_quantize_pack.restype, l.rc_quantize_pack.argtypes = i32, [Codec, i32, vp, sz, vp, vp]
+    l.rc_unpack_dequant.restype, l.rc_unpack_dequant.argtypes = i32, [Codec, vp, sz, i32, vp, vp]
+    l.rc_dequant_reduce_requant.restype = i32
+    l.rc_dequant_reduce_requant.argtypes = [Codec, ctypes.POINTER(vp), i32, sz, vp, vp, vp]
+    l.rc_copy.restype, l.rc_copy.argtypes = i32, [vp, vp, sz, vp]
+    l.rc_status_str.restype, l.rc_status_str.argtypes = ctypes.c_char_p, [i32]
+    l.rc_abi_version.restype, l.rc_abi_version.argtypes = i32, []
+    _lib = l
+    return l
+
+
+def _codec(c) -> Codec:
+    if isinstance(c, Codec):
+        return c
+    if isinstance(c, str):
+        return CODECS[c]
+    return Codec(*c)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ok(status: int, what: str):
+    if status != OK:
+        raise CodecError(status, what)
+
+
+def tile_bytes(codec) -> int:
+    return lib().rc_tile_bytes(_codec(codec))
+
+
+def packed_bytes(codec, n: int) -> int:
+    return lib().rc_packed_bytes(_codec(codec), n)
+
+
+def quantize_pack(x: torch.Tensor, codec, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Block-quantize the elements of x (bf16 / fp16 / fp32, any shape, taken
+    flat) into ``packed_bytes(codec, x.numel())`` bytes."""
+    c = _codec(codec)
+    _check_dev(x, "x")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    n = x.numel()
+    if out is None:
+        out = torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=x.device)
+    _check_dev(out, "out")
+    if out.numel() < packed_bytes(c, n) or out.dtype != torch.uint8:
+        raise ValueError("out must be a uint8 tensor of packed_bytes(codec, n) bytes")
+    _ok(lib().rc_quantize_pack(c, _DTYPES[x.dtype], x.data_ptr(), n, out.data_ptr(), _stream(stream)),
+        "rc_quantize_pack")
+    return out
+
+
+def unpack_dequant(packed: torch.Tensor, codec, n: int, dtype: torch.dtype = torch.float32,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode the first n elements of a packed stream to dtype."""
+    c = _codec(codec)
+    _check_dev(packed, "packed")
+    if packed.numel() < packed_bytes(c, n):
+        raise ValueError("packed is shorter than packed_bytes(codec, n)")
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported output dtype {dtype}")
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=packed.device)
+    _check_dev(out, "out")
+    if out.numel() < n or out.dtype != dtype:
+        raise ValueError("out must hold n elements of dtype")
+    _ok(lib().rc_unpack_dequant(c, packed.data_ptr(), n, _DTYPES[dtype], out.data_ptr(), _stream(stream)),
+        "rc_unpack_dequant")
+    return out
+
+
+def dequant_reduce_requant(streams, codec, n: int, out: torch.Tensor | None = None,
+                           sum_out: bool | torch.Tensor = False, stream=None):
+    """Dequantize K packed streams, add them in FP32 in stream order and
+    requantize.  Returns (packed, sums) with sums None unless requested."""
+    c = _codec(codec)
+    streams = list(streams)
+    k = len(streams)
+    if not 1 <= k <= MAX_STREAMS:
+        raise ValueError(f"need 1..{MAX_STREAMS} streams, got {k}")
+    need = packed_bytes(c, n)
+    for j, s in enumerate(streams):
+        _check_dev(s, f"streams[{j}]")
+        if s.numel() < need:
+            raise ValueError(f"streams[{j}] is shorter than packed_bytes(codec, n)")
+    dev = streams[0].device
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check_dev(out, "out")
+    sums = None
+    if isinstance(sum_out, torch.Tensor):
+        sums = sum_out
+        _check_dev(sums, "sum_out")
+        if sums.dtype != torch.float32 or sums.numel() < n:
+            raise ValueError("sum_out must hold n float32 values")
+    elif sum_out:
+        sums = torch.empty(n, dtype=torch.float32, device=dev)
+    ptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in streams])
+    _ok(lib().rc_dequant_reduce_requant(c, ptrs, k, n, out.data_ptr(),
+                                        sums.data_ptr() if sums is not None else None, _stream(stream)),
+        "rc_dequant_reduce_requant")
+    return out, sums
+
+
+def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> torch.Tensor:
+    """Byte copy through the library's 16-byte vector copy kernel."""
+    _check_dev(dst, "dst")
+    _check_dev(src, "src")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _ok(lib().rc_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)), "rc_copy")
+    return dst

@@ -1,0 +1,112 @@
+// rc_api.cpp -- the C ABI of librcodec.so (declared in include/rcodec.h):
+// argument validation, then one kernel launch on the caller's stream.
+// Validation never touches HIP, so every error path can be exercised on a
+// machine without a GPU.
+#include "rcodec.h"
+#include "rc_internal.hpp"
+
+namespace {
+
+// Largest n accepted: 2^40 elements keeps every tile index, byte offset and
+// grid dimension (tiles / 4 workgroups) far inside their types.
+constexpr size_t kMaxElems = (size_t)1 << 40;
+
+bool codec_ok(rc_codec c)
+{
+    if (c.block != RC_BLOCK_ELEMS) return false;
+    switch (c.format) {
+    case RC_FMT_INT4:     return c.scale == RC_SCALE_FP16;
+    case RC_FMT_INT3:     return c.scale == RC_SCALE_FP16;
+    case RC_FMT_FP8_E4M3: return c.scale == RC_SCALE_FP32;
+    case RC_FMT_MXFP4:    return c.scale == RC_SCALE_E8M0;
+    default:              return false;
+    }
+}
+
+bool dtype_ok(int d) { return d == RC_DT_FP32 || d == RC_DT_FP16 || d == RC_DT_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+rc_status from_hip(hipError_t e) { return e == hipSuccess ? RC_OK : RC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t rc_tile_bytes(rc_codec c)
+{
+    if (!codec_ok(c)) return 0;
+    switch (c.format) {
+    case RC_FMT_INT4:     return 1152;
+    case RC_FMT_INT3:     return 896;
+    case RC_FMT_FP8_E4M3: return 2304;
+    default:              return 1088;
+    }
+}
+
+size_t rc_packed_bytes(rc_codec c, size_t n)
+{
+    return ((n + RC_TILE_ELEMS - 1) / RC_TILE_ELEMS) * rc_tile_bytes(c);
+}
+
+rc_status rc_quantize_pack(rc_codec c, rc_dtype in_t, const void* in, size_t n, void* out, void* stream)
+{
+    if (!codec_ok(c) || !dtype_ok(in_t)) return RC_ERR_UNSUPPORTED;
+    if (n == 0) return RC_OK;
+    if (n > kMaxElems) return RC_ERR_RANGE;
+    if (!in || !out) return RC_ERR_NULL;
+    if (!aligned16(in) || !aligned16(out)) return RC_ERR_ALIGN;
+    return from_hip(rc::launch_quantize(c.format, in_t, in, n, out, static_cast<hipStream_t>(stream)));
+}
+
+rc_status rc_unpack_dequant(rc_codec c, const void* in, size_t n, rc_dtype out_t, void* out, void* stream)
+{
+    if (!codec_ok(c) || !dtype_ok(out_t)) return RC_ERR_UNSUPPORTED;
+    if (n == 0) return RC_OK;
+    if (n > kMaxElems) return RC_ERR_RANGE;
+    if (!in || !out) return RC_ERR_NULL;
+    if (!aligned16(in) || !aligned16(out)) return RC_ERR_ALIGN;
+    return from_hip(rc::launch_unpack(c.format, in, n, out_t, out, static_cast<hipStream_t>(stream)));
+}
+
+rc_status rc_dequant_reduce_requant(rc_codec c, const void* const* ins, int k, size_t n, void* out,
+                                    float* sum_out, void* stream)
+{
+    if (!codec_ok(c)) return RC_ERR_UNSUPPORTED;
+    if (k < 1 || k > RC_MAX_STREAMS) return RC_ERR_RANGE;
+    if (n == 0) return RC_OK;
+    if (n > kMaxElems) return RC_ERR_RANGE;
+    if (!ins || !out) return RC_ERR_NULL;
+    rc::StreamPtrs p = {};
+    for (int j = 0; j < k; ++j) {
+        if (!ins[j]) return RC_ERR_NULL;
+        if (!aligned16(ins[j])) return RC_ERR_ALIGN;
+        p.p[j] = static_cast<const uint8_t*>(ins[j]);
+    }
+    if (!aligned16(out) || (sum_out && !aligned16(sum_out))) return RC_ERR_ALIGN;
+    return from_hip(rc::launch_reduce(c.format, p, k, n, out, sum_out, static_cast<hipStream_t>(stream)));
+}
+
+rc_status rc_copy(const void* in, void* out, size_t bytes, void* stream)
+{
+    if (bytes == 0) return RC_OK;
+    if (!in || !out) return RC_ERR_NULL;
+    if (!aligned16(in) || !aligned16(out) || (bytes & 15u)) return RC_ERR_ALIGN;
+    return from_hip(rc::launch_copy(in, out, bytes, static_cast<hipStream_t>(stream)));
+}
+
+const char* rc_status_str(rc_status s)
+{
+    switch (s) {
+    case RC_OK:              return "ok";
+    case RC_ERR_NULL:        return "null pointer";
+    case RC_ERR_UNSUPPORTED: return "unsupported codec or dtype";
+    case RC_ERR_ALIGN:       return "pointer not 16-byte aligned";
+    case RC_ERR_RANGE:       return "argument out of range";
+    case RC_ERR_HIP:         return "HIP launch failed";
+    default:                 return "unknown status";
+    }
+}
+
+int rc_abi_version(void) { return RC_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Packed codes and scales must be bit-exact; the FP32 sums of the reduce are
+compared bit for bit as well (the stated tolerance, 1e-6 relative, is also
+asserted so a failure reports how far off it is).  Oracle inputs always come
+from the seeded generators or from the oracle itself, never from the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import reduction_codec_amd as rca
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+FMTS = ["int4", "int3", "fp8", "mxfp4"]
+DTYPES = ["bf16", "fp16", "fp32"]
+TORCH_DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+ORACLE_DT = {"bf16": oracle.DT_BF16, "fp16": oracle.DT_FP16, "fp32": oracle.DT_FP32}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray, dt: str) -> torch.Tensor:
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host_u8(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint8)
+
+
+def mixed(n: int, seed: int, dt: str) -> np.ndarray:
+    """float32 values covering the cases that take the exact path: zero and
+    negative-zero blocks, ties at half steps, grid values, tiny blocks with
+    subnormal fp16 scales, saturating blocks, denormals -- then narrowed to
+    dt (kept inside dt's finite range)."""
+    r = np.random.default_rng(seed)
+    v = r.standard_normal(n).astype(np.float32)
+    blocks = max(1, n // 32)
+    kinds = r.integers(0, 10, blocks)
+    for b in range(blocks):
+        sl = slice(32 * b, min(n, 32 * b + 32))
+        m = sl.stop - sl.start
+        k = kinds[b]
+        if k == 0:
+            v[sl] = 0.0
+            v[sl.start] = -0.0
+        elif k == 1:
+            step = np.float32(2.0 ** r.integers(-6, 6))
+            v[sl] = (r.integers(-7, 8, m) * step / 2).astype(np.float32)        # half-step ties
+            v[sl.start] = 7 * step
+        elif k == 2:
+            v[sl] *= np.float32(1e-5)
+        elif k == 3:
+            v[sl] *= np.float32(3e-8)
+        elif k == 4:
+            v[sl] *= np.float32(2e5)
+        elif k == 5:
+            v[sl] = (r.integers(-3, 4, m) * 0.25).astype(np.float32)
+            v[sl.start] = 0.75
+        elif k == 6:
+            v[sl] *= np.float32(50)
+    if dt == "fp16":
+        v = np.clip(v, -60000, 60000).astype(np.float32)
+    return datagen.narrow(v, dt)
+
+
+def assert_same(got: np.ndarray, ref: np.ndarray, what: str):
+    """Bitwise equality of two arrays of the same dtype; on failure report the
+    first differing positions with both values."""
+    g = np.ascontiguousarray(got)
+    r = np.ascontiguousarray(ref)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    bad = np.nonzero(g.view(np.uint8).reshape(g.size, -1).any(axis=1) if False else
+                     (g.view(np.uint8).reshape(g.size, -1) != r.view(np.uint8).reshape(r.size, -1)).any(axis=1))[0]
+    if bad.size:
+        show = [(int(i), g[i], r[i]) for i in bad[:8]]
+        raise AssertionError(f"{what}: {bad.size} of {g.size} differ; first (index, got, ref): {show}")
+
+
+def oracle_pack(fmt, x, dt):
+    return oracle.quantize_pack(oracle.CODECS[fmt], x, dtype=ORACLE_DT[dt])
+
+
+# ------------------------------------------------------------ quantize ----
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 2047, 2048, 2049, 5 * 2048 + 777])
+def test_quantize_pack_bit_exact(fmt, dt, n):
+    say(f"case quantize fmt={fmt} dt={dt} n={n}")
+    x = mixed(n, seed=n * 7 + len(fmt), dt=dt)
+    ref = oracle_pack(fmt, x, dt)
+    pb = rca.packed_bytes(rca.CODECS[fmt], n)
+    buf = torch.full((pb + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    rca.quantize_pack(to_dev(x, dt), rca.CODECS[fmt], out=buf[:pb])
+    got = host_u8(buf)
+    assert np.array_equal(got[:pb], ref)
+    assert (got[pb:] == 0xA5).all(), "wrote past the packed size"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_is_deterministic(fmt):
+    x = mixed(40 * 2048 + 5, 3, "bf16")
+    xt = to_dev(x, "bf16")
+    a = rca.quantize_pack(xt, rca.CODECS[fmt]).clone()
+    b = rca.quantize_pack(xt, rca.CODECS[fmt])
+    assert torch.equal(a, b)
+
+
+# -------------------------------------------------------------- unpack ----
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("odt", DTYPES)
+def test_unpack_dequant_bit_exact(fmt, odt):
+    n = 6 * 2048 + 99
+    say(f"case unpack fmt={fmt} odt={odt} n={n}")
+    x = mixed(n, 11, "fp32")
+    packed = oracle_pack(fmt, x, "fp32")
+    ref = oracle.unpack_dequant(oracle.CODECS[fmt], packed, n, ORACLE_DT[odt])
+    esz = 4 if odt == "fp32" else 2
+    buf = torch.full((n * esz + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+    out = buf[:n * esz].view(TORCH_DT[odt])
+    rca.unpack_dequant(torch.from_numpy(packed).to(DEV), rca.CODECS[fmt], n, TORCH_DT[odt], out=out)
+    got = host_u8(buf)
+    assert_same(got[:n * esz].view(np.asarray(ref).dtype), ref, f"unpack {fmt}->{odt}")
+    assert (got[n * esz:] == 0x5A).all()
+
+
+# -------------------------------------------------------------- reduce ----
+
+def oracle_streams(fmt, n, k, seed):
+    out = []
+    for j in range(k):
+        x = mixed(n, seed + 13 * j, "fp32") if j % 2 == 0 else \
+            (np.random.default_rng(seed + j).standard_normal(n) * (j + 1)).astype(np.float32)
+        out.append(oracle_pack(fmt, x, "fp32"))
+    return out
+
+
+def assert_sums(got: np.ndarray, ref: np.ndarray):
+    same = got.view(np.uint32) == ref.view(np.uint32)
+    both_nan = np.isnan(got) & np.isnan(ref)
+    ok = same | both_nan
+    if not ok.all():
+        rel = np.abs(got.astype(np.float64) - ref) / np.maximum(np.abs(ref.astype(np.float64)), 1e-300)
+        raise AssertionError(f"{(~ok).sum()} sums differ; max rel {np.nanmax(rel):.3g} (bound 1e-6)")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 8, 16])
+def test_reduce_bit_exact(fmt, k):
+    n = 3 * 2048 + 500
+    say(f"case reduce fmt={fmt} k={k} n={n}")
+    streams = oracle_streams(fmt, n, k, seed=100 * k)
+    ref, ref_sum = oracle.dequant_reduce_requant(oracle.CODECS[fmt], streams, n, want_sum=True)
+    dev_streams = [torch.from_numpy(s).to(DEV) for s in streams]
+    pb = rca.packed_bytes(rca.CODECS[fmt], n)
+    buf = torch.full((pb + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    out, sums = rca.dequant_reduce_requant(dev_streams, rca.CODECS[fmt], n, out=buf[:pb], sum_out=True)
+    got = host_u8(buf)
+    assert np.array_equal(got[:pb], ref)
+    assert (got[pb:] == 0xA5).all()
+    assert_sums(sums.cpu().numpy(), ref_sum)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_reduce_ignores_tail_codes(fmt):
+    n = 2048 + 40
+    streams = oracle_streams(fmt, n, 2, seed=5)
+    tb = oracle.tile_bytes(oracle.CODECS[fmt])
+    rng = np.random.default_rng(0)
+    junk = streams[0].copy()
+    if fmt == "int3":
+        junk[tb + 16:tb + 512] = rng.integers(0, 256, 496, dtype=np.uint8)
+        junk[tb + 520:tb + 768] = rng.integers(0, 256, 248, dtype=np.uint8)
+    elif fmt == "fp8":
+        junk[tb + 64:tb + 2048] = rng.integers(0, 127, 1984, dtype=np.uint8)
+    else:
+        junk[tb + 32:tb + 1024] = rng.integers(0, 256, 992, dtype=np.uint8)
+    ref, _ = oracle.dequant_reduce_requant(oracle.CODECS[fmt], [junk, streams[1]], n)
+    out, _ = rca.dequant_reduce_requant([torch.from_numpy(junk).to(DEV), torch.from_numpy(streams[1]).to(DEV)],
+                                        rca.CODECS[fmt], n)
+    assert np.array_equal(host_u8(out), ref)
+
+
+def test_zero_length_and_errors_on_gpu():
+    x = torch.zeros(0, dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    assert rca.lib().rc_quantize_pack(rca.INT3, rca.DT_BF16, x.data_ptr(), 0, out.data_ptr(), None) == rca.OK
+    with pytest.raises(rca.CodecError):
+        rca.dequant_reduce_requant([out], rca.Codec(2, 2, 32), 0)
+
+
+# -------------------------------------------------------- configurations ----
+
+def test_config_int4_fp16_64_tiles_roundtrip_and_k2():
+    """64 tiles x 2048 fp16 ~ N(0,1) (seeds 0, 1): INT4 pack, 2-stream reduce, unpack."""
+    xs = [datagen.fp16_normal_64x2048(s) for s in (0, 1)]
+    n = xs[0].size
+    refs = [oracle_pack("int4", x, "fp16") for x in xs]
+    for x, ref in zip(xs, refs):
+        got = host_u8(rca.quantize_pack(to_dev(x, "fp16"), rca.INT4))
+        assert np.array_equal(got, ref)
+        assert got.size == 64 * 1152
+    ref, ref_sum = oracle.dequant_reduce_requant(oracle.INT4, refs, n, want_sum=True)
+    out, sums = rca.dequant_reduce_requant([torch.from_numpy(r).to(DEV) for r in refs], rca.INT4, n,
+                                           sum_out=True)
+    assert np.array_equal(host_u8(out), ref)
+    assert_sums(sums.cpu().numpy(), ref_sum)
+    y = rca.unpack_dequant(out, rca.INT4, n, torch.float16)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16),
+                          oracle.unpack_dequant(oracle.INT4, ref, n, oracle.DT_FP16).view(np.uint16))
+
+
+def test_config_int3_bf16_activation_4mb():
+    """256 x 8192 bf16 activation, N(0,1) with 0.1% outliers x20: INT3 pack,
+    unpack, and a 4-stream reduce of the message and three tile-shifted copies."""
+    x = datagen.bf16_act_256x8192_outl()
+    n = x.size
+    ref = oracle.quantize_pack_parallel(oracle.INT3, x, dtype=oracle.DT_BF16)
+    got = host_u8(rca.quantize_pack(to_dev(x, "bf16"), rca.INT3))
+    assert np.array_equal(got, ref) and got.size == 1024 * 896
+    y = rca.unpack_dequant(torch.from_numpy(ref).to(DEV), rca.INT3, n, torch.bfloat16)
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16),
+                          oracle.unpack_dequant(oracle.INT3, ref, n, oracle.DT_BF16))
+    tb = 896
+    streams = [np.roll(ref.reshape(-1, tb), j, axis=0).ravel().copy() for j in range(4)]
+    rref, rsum = oracle.dequant_reduce_requant_parallel(oracle.INT3, streams, n, want_sum=True)
+    out, sums = rca.dequant_reduce_requant([torch.from_numpy(s).to(DEV) for s in streams], rca.INT3, n,
+                                           sum_out=True)
+    assert np.array_equal(host_u8(out), rref)
+    assert_sums(sums.cpu().numpy(), rsum)
+
+
+def test_config_fp8_eight_fp32_streams_16mb():
+    """8 fp32 streams of 4M elements ~ N(0, 0.5): FP8 pack each, K=8 reduce."""
+    n = 4 * 1024 * 1024
+    refs = []
+    for k in range(8):
+        say(f"case fp8 config stream {k}")
+        x = datagen.fp32_normal_4m(k)
+        ref = oracle.quantize_pack_parallel(oracle.FP8, x)
+        got = host_u8(rca.quantize_pack(to_dev(x, "fp32"), rca.FP8))
+        assert np.array_equal(got, ref)
+        refs.append(ref)
+    say("case fp8 config reduce k=8")
+    rref, rsum = oracle.dequant_reduce_requant_parallel(oracle.FP8, refs, n, want_sum=True)
+    out, sums = rca.dequant_reduce_requant([torch.from_numpy(r).to(DEV) for r in refs], rca.FP8, n,
+                                           sum_out=True)
+    assert np.array_equal(host_u8(out), rref)
+    assert_sums(sums.cpu().numpy(), rsum)
+    # 4:1 payload: code bytes are a quarter of the fp32 input bytes
+    assert (n // 2048) * 2048 * 4 / ((n // 2048) * 2048) == 4
+
+
+def test_config_mxfp4_bf16_weight_4096():
+    """bf16 4096x4096 weight, 0.02 N(0,1) with U[0.5,2] row drift: MXFP4 pack and unpack."""
+    x = datagen.bf16_weight_4096x4096()
+    n = x.size
+    ref = oracle.quantize_pack_parallel(oracle.MXFP4, x, dtype=oracle.DT_BF16)
+    got = host_u8(rca.quantize_pack(to_dev(x, "bf16"), rca.MXFP4))
+    assert np.array_equal(got, ref) and got.size == 8192 * 1088
+    y = rca.unpack_dequant(torch.from_numpy(ref).to(DEV), rca.MXFP4, n, torch.bfloat16)
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16),
+                          oracle.unpack_dequant(oracle.MXFP4, ref, n, oracle.DT_BF16))
+
+
+# ----------------------------------------- size sweep, sampled tiles ----
+
+SWEEP_MIB = [1, 4, 16, 64, 256, 1024]
+
+
+def sample_tiles(tiles: int, rng) -> list:
+    pick = {0, tiles - 1, tiles // 2}
+    pick.update(int(t) for t in rng.integers(0, tiles, 40))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("mib", SWEEP_MIB)
+@pytest.mark.parametrize("fmt", ["int4", "int3"])
+def test_sweep_sampled_tiles(fmt, mib):
+    """Student-t (nu=4) bf16 messages at full size in the launch shape the
+    benchmark uses: quantize_pack of the message and a K=4 reduce of four
+    tile-shifted messages, checked on sampled tiles the oracle computes."""
+    n = mib * (1 << 20) // 2
+    say(f"case sweep fmt={fmt} size={mib}MiB")
+    base = datagen.bf16_student4(mib * (1 << 20) + 3 * 4096)        # n + 3 tiles
+    streams_x = [base[j * 2048: j * 2048 + n] for j in range(4)]
+    c, oc = rca.CODECS[fmt], oracle.CODECS[fmt]
+    tb = oracle.tile_bytes(oc)
+    tiles = -(-n // 2048)
+    rng = np.random.default_rng(mib)
+    picks = sample_tiles(tiles, rng)
+    dev_packed = []
+    ref_packed = []
+    for j, xs in enumerate(streams_x):
+        p = rca.quantize_pack(to_dev(xs, "bf16"), c)
+        dev_packed.append(p)
+        refp = np.zeros(oracle.packed_bytes(oc, n), dtype=np.uint8)
+        for t in picks:
+            oracle.quantize_pack(oc, xs, dtype=oracle.DT_BF16, tiles=(t, t + 1), out=refp)
+        hp = host_u8(p)
+        for t in picks:
+            assert np.array_equal(hp[t * tb:(t + 1) * tb], refp[t * tb:(t + 1) * tb]), f"stream {j} tile {t}"
+        ref_packed.append(refp)
+    out, _ = rca.dequant_reduce_requant(dev_packed, c, n)
+    hout = host_u8(out)
+    refo = np.zeros_like(ref_packed[0])
+    for t in picks:
+        oracle.dequant_reduce_requant(oc, ref_packed, n, tiles=(t, t + 1), out=refo)
+        assert np.array_equal(hout[t * tb:(t + 1) * tb], refo[t * tb:(t + 1) * tb]), f"reduce tile {t}"
+    del dev_packed, out
+    torch.cuda.empty_cache()
