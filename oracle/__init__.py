@@ -68,7 +68,8 @@ def _load():
         "rco_e8m0_decode": (ctypes.c_float, [ctypes.c_uint8]),
         "rco_e4m3_mag_of_quotient": (i32, [ctypes.c_double, ctypes.c_double]),
         "rco_e2m1_mag_of": (i32, [ctypes.c_double]),
-        "rco_int_mag_of_quotient": (i32, [ctypes.c_double, ctypes.c_double, i32]),
+        "rco_int_recip": (ctypes.c_float, [ctypes.c_float]),
+        "rco_int_mag_recip": (i32, [ctypes.c_float, ctypes.c_float, i32]),
         "rco_int_scale_bits": (ctypes.c_uint16, [ctypes.c_float, i32]),
         "rco_fp8_scale": (ctypes.c_float, [ctypes.c_float]),
         "rco_mx_exponent": (i32, [ctypes.c_float]),
@@ -232,12 +233,12 @@ def e2m1_mag_of(v):
     return _map("rco_map_e2m1_mag", np.int32, np.asarray(v, dtype=np.float64))
 
 
-def int_mag_of_quotient(num, den, qmax):
-    num = np.asarray(num, dtype=np.float64)
-    den = np.broadcast_to(np.asarray(den, dtype=np.float64), num.shape)
-    a = [np.ascontiguousarray(num), np.ascontiguousarray(den)]
-    out = np.empty(num.size, dtype=np.int32)
-    _load().rco_map_int_mag(_ptr(a[0]), _ptr(a[1]), qmax, _ptr(out), num.size)
+def int_mag(v_abs, s, qmax):
+    """min(RNE(RN32(|v| * RN32(1/s))), qmax) element-wise (float32 inputs)."""
+    v_abs = np.ascontiguousarray(v_abs, dtype=np.float32)
+    s = np.ascontiguousarray(np.broadcast_to(np.asarray(s, dtype=np.float32), v_abs.shape))
+    out = np.empty(v_abs.size, dtype=np.int32)
+    _load().rco_map_int_mag(_ptr(v_abs), _ptr(s), qmax, _ptr(out), v_abs.size)
     return out
 
 

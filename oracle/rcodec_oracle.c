@@ -13,6 +13,8 @@
  * Layout of one 2048-element tile (32-element blocks b = 0..63; element i of
  * the tile lies in block i/32 at position e = i%32):
  *
+ * INT codes use the reciprocal rule: magnitude = min(RNE(RN32(|v| * RN32(1/s))), qmax).
+ *
  *   INT4 (1152 B):  nibble i of bytes [0,1024) (low nibble first) holds
  *                   (sign << 3) | magnitude, magnitude 0..7;
  *                   fp16 scale of block b at 1024 + 2b.
@@ -205,22 +207,28 @@ int rco_e2m1_mag_of(double y_abs)
     return nearest_of_quotient(e2m1_mag, 8, y_abs, 1.0);
 }
 
-/* Symmetric integer magnitude: the integer nearest to num/den, ties to even,
- * clamped to qmax ("symmetric quantization", QuickReduce INT3 ... -- Method).
- * num is |v| for a binary32 v, den an fp16 value.  Below the clamp k <= 7, so
- * k*den and (k+1/2)*den = (2k+1)*den/2 have at most 15 significant bits and
- * are exact in binary64; every comparison below is therefore exact. */
-int rco_int_mag_of_quotient(double num, double den, int qmax)
+/* Reciprocal of a nonzero INT block scale: one IEEE binary32 division. */
+float rco_int_recip(float s)
 {
-    if (num >= (qmax + 0.5) * den) return qmax;       /* RNE then clamp */
-    int k = (int)floor(num / den);                    /* candidate      */
-    while (k > 0 && k * den > num) --k;                /* make k*den <= num */
-    while ((k + 1) * den <= num) ++k;                  /* < (k+1)*den    */
-    double mid = (k + 0.5) * den;
+    return 1.0f / s;
+}
+
+/* Symmetric integer magnitude ("symmetric quantization", QuickReduce INT3 ...
+ * -- Method), by the reciprocal rule: y = RN32(|v| * r) with r = RN32(1/s),
+ * one binary32 multiplication, then the integer nearest to y with ties to
+ * even, clamped to qmax.  y is a binary32 value, so floor(y) and y - floor(y)
+ * are exact in binary64 and every comparison below is exact. */
+int rco_int_mag_recip(float v_abs, float r, int qmax)
+{
+    const float y = v_abs * r;
+    const double yd = (double)y;
+    if (yd >= qmax + 0.5) return qmax;                 /* RNE, then clamp */
+    const int k = (int)floor(yd);
+    const double frac = yd - (double)k;
     int m;
-    if (num > mid)      m = k + 1;
-    else if (num < mid) m = k;
-    else                m = (k % 2 == 0) ? k : k + 1;
+    if (frac > 0.5)      m = k + 1;
+    else if (frac < 0.5) m = k;
+    else                 m = (k % 2 == 0) ? k : k + 1;
     return m > qmax ? qmax : m;
 }
 
@@ -336,9 +344,10 @@ static void encode_tile(rco_codec c, const float *v, uint8_t *dst)
             float s = rco_f16_to_f32(h);
             if (s == 0.0f) continue;                 /* zero block: all bytes 0 */
             put_u16(dst + (c.format == RCO_FMT_INT4 ? 1024 : 768) + 2 * b, h);
+            const float r = rco_int_recip(s);
             for (int e = 0; e < 32; ++e) {
                 unsigned sign = signbit(vb[e]) ? 1u : 0u;
-                unsigned mag = (unsigned)rco_int_mag_of_quotient(fabs((double)vb[e]), s, qmax);
+                unsigned mag = (unsigned)rco_int_mag_recip(fabsf(vb[e]), r, qmax);
                 size_t i = (size_t)32 * b + e;
                 if (c.format == RCO_FMT_INT4) {
                     put_bits(dst, 4 * i, (sign << 3) | mag, 4);
@@ -504,8 +513,8 @@ void rco_map_e4m3_mag(const double *num, const double *den, int32_t *y, size_t n
 { for (size_t i = 0; i < n; ++i) y[i] = rco_e4m3_mag_of_quotient(num[i], den[i]); }
 void rco_map_e2m1_mag(const double *v, int32_t *y, size_t n)
 { for (size_t i = 0; i < n; ++i) y[i] = rco_e2m1_mag_of(v[i]); }
-void rco_map_int_mag(const double *num, const double *den, int qmax, int32_t *y, size_t n)
-{ for (size_t i = 0; i < n; ++i) y[i] = rco_int_mag_of_quotient(num[i], den[i], qmax); }
+void rco_map_int_mag(const float *v_abs, const float *s, int qmax, int32_t *y, size_t n)
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_int_mag_recip(v_abs[i], rco_int_recip(s[i]), qmax); }
 void rco_map_int_scale_bits(const float *amax, int qmax, uint16_t *y, size_t n)
 { for (size_t i = 0; i < n; ++i) y[i] = rco_int_scale_bits(amax[i], qmax); }
 void rco_map_fp8_scale(const float *amax, float *y, size_t n)

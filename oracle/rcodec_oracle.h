@@ -7,7 +7,8 @@
  *
  * What it computes (the spec of record, one definition per step):
  *   - block quantization with one scale per 32-element block, symmetric
- *     integer codes and an FP16 block scale, the 3-bit codes split into a
+ *     integer codes (|v| times the binary32 reciprocal of the scale, rounded
+ *     half-even) and an FP16 block scale, the 3-bit codes split into a
  *     low-2-bit plane (q2w) and a high-bit plane (q1w)
  *       [QuickReduce INT3 Quantization and Benchmarking on MI355 -- Method];
  *   - fixed 2048-element tiles that pack to 1152 B (INT4) and 896 B (INT3)
@@ -81,7 +82,10 @@ float    rco_e8m0_decode(uint8_t byte);           /* 2^(byte-127), 0xFF NaN */
  * saturating; num, den exact doubles, den > 0 */
 int      rco_e4m3_mag_of_quotient(double num, double den);   /* 0..126 */
 int      rco_e2m1_mag_of(double y_abs);                      /* 0..7   */
-int      rco_int_mag_of_quotient(double num, double den, int qmax);
+/* INT magnitude by the reciprocal rule: min(RNE(RN32(v_abs * r)), qmax),
+ * r = rco_int_recip(s) = RN32(1/s) */
+float    rco_int_recip(float s);
+int      rco_int_mag_recip(float v_abs, float r, int qmax);
 /* per-block scale rules; amax >= 0 */
 uint16_t rco_int_scale_bits(float amax, int qmax);   /* fp16 bits       */
 float    rco_fp8_scale(float amax);                  /* 0 when flushed  */
@@ -94,7 +98,7 @@ void rco_map_f16_to_f32(const uint16_t *x, float *y, size_t n);
 void rco_map_bf16_to_f32(const uint16_t *x, float *y, size_t n);
 void rco_map_e4m3_mag(const double *num, const double *den, int32_t *y, size_t n);
 void rco_map_e2m1_mag(const double *v, int32_t *y, size_t n);
-void rco_map_int_mag(const double *num, const double *den, int qmax, int32_t *y, size_t n);
+void rco_map_int_mag(const float *v_abs, const float *s, int qmax, int32_t *y, size_t n);
 void rco_map_int_scale_bits(const float *amax, int qmax, uint16_t *y, size_t n);
 void rco_map_fp8_scale(const float *amax, float *y, size_t n);
 void rco_map_mx_exponent(const float *amax, int32_t *y, size_t n);

@@ -39,8 +39,10 @@ def nearest_code(q: Fraction, table) -> int:
 
 
 def int_mag(v: float, s: float, qmax: int) -> int:
-    q = Fraction(abs(float(v))) / Fraction(float(s))
-    return nearest_code(q, [Fraction(k) for k in range(qmax + 1)])
+    """Reciprocal rule: y = fp32(|v| * fp32(1/s)) by numpy float32 arithmetic,
+    then the nearest of 0..qmax in exact rationals, ties to even."""
+    y = np.float32(abs(np.float32(v))) * (np.float32(1.0) / np.float32(s))
+    return nearest_code(Fraction(float(y)), [Fraction(k) for k in range(qmax + 1)])
 
 
 def int_scale(a: np.float32, qmax: int) -> np.float16:
