@@ -10,15 +10,15 @@
 // (E4M3) conversion instructions:
 //   * INT3 magnitudes 0..3 are the E2M1 codes of 0, 0.5, 1, 1.5, so a
 //     sign/magnitude INT3 code is an E2M1 nibble of value q/2 with bit 2
-//     clear.  Quantize = E2M1 conversion of x/(2s); dequantize = E2M1
-//     conversion back, times 2s.
+//     clear.  Quantize = E2M1 conversion of x * (r/2), r = fp32(1/s);
+//     dequantize = E2M1 conversion back, times 2s.
 //   * INT4 magnitudes 0..7 are the E4M3 subnormals m * 2^-9, so a sign /
 //     magnitude INT4 code is an E4M3 byte with exponent 0.
-// The conversions round the binary32 product x * (1/(2s)) to nearest even;
-// the exact-quotient rule of the format is then enforced by an exact residual
-// check |x - q s| < s/2 per element, and any block that fails it (a value
-// within rounding distance of a half-integer step, a tie, a subnormal or
-// saturated scale) is recomputed by an exact comparison path.
+// Both conversions round their binary32 input to nearest even, which is the
+// INT rounding rule itself: magnitude = RNE(fp32(|x| * fp32(1/s))).  For a
+// normal, unsaturated fp16 scale |x| * r <= qmax + 0.004, so no clamp is
+// needed; blocks with a subnormal or saturated scale are re-encoded with a
+// clamp behind a (rarely taken) branch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -148,8 +148,9 @@ __device__ __forceinline__ float absmax32(const float (&v)[32])
 struct IntScale {
     float s;          // fp16 scale as binary32 (exact)
     uint32_t bits;    // fp16 bit pattern
+    float r;          // fp32(1/s) (IEEE division), 0 for a zero block
     bool zero;        // s == 0: the block is stored as zeros
-    bool abnormal;    // subnormal fp16 or saturated: exact path only
+    bool abnormal;    // subnormal fp16 or saturated: codes need the clamp
 };
 
 // s = fp16(min(fp32(a / qmax), 65504)); fp32 division is the IEEE one.
@@ -165,21 +166,8 @@ __device__ __forceinline__ IntScale int_scale(float a)
     r.s = __half2float(h);
     r.zero = (r.s == 0.0f);
     r.abnormal = sat || (!r.zero && r.s < 0x1p-14f);
+    r.r = r.zero ? 0.0f : 1.0f / r.s;
     return r;
-}
-
-// Exact symmetric magnitude min(RNE(ax / s), QMAX) by comparison with the
-// exact half-step thresholds (2k+1) s / 2 (at most 15 significant bits).
-template <int QMAX>
-__device__ __forceinline__ uint32_t int_mag_exact(float ax, float s)
-{
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < QMAX; ++k) {
-        float t = ((float)(2 * k + 1) * s) * 0.5f;
-        m += (ax > t || (ax == t && (k & 1))) ? 1u : 0u;
-    }
-    return m;
 }
 
 __device__ __forceinline__ uint32_t signbit_u(float x) { return __float_as_uint(x) >> 31; }
@@ -209,16 +197,22 @@ __device__ __forceinline__ uint32_t int3_group(uint32_t w0, uint32_t w1, uint32_
     return ((w >> (2 * (g & 1))) & 0x33333333u) | ((h << (3 - g)) & 0x88888888u);
 }
 
-__device__ __forceinline__ void int3_exact_groups(const float (&v)[32], float s, bool zero, uint32_t (&N)[4])
+// E2M1 nibbles of the 32 elements, group g in word N[g] (nibble j = element
+// 4j + g), of x * r2 with r2 = fp32(1/s) / 2, clamped to +-1.5 if CLAMP.
+template <bool CLAMP>
+__device__ __forceinline__ void int3_groups(const float (&v)[32], float r2, uint32_t (&N)[4])
 {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        uint32_t w = 0;
+        uint32_t w = 0u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float x = v[4 * j + g];
-            uint32_t c = (signbit_u(x) << 3) | int_mag_exact<3>(fabsf(x), s);
-            w |= (zero ? 0u : c) << (4 * j);
+        for (int b = 0; b < 4; ++b) {
+            float ya = v[8 * b + g] * r2, yb = v[8 * b + 4 + g] * r2;
+            if (CLAMP) {
+                ya = fminf(fmaxf(ya, -1.5f), 1.5f);
+                yb = fminf(fmaxf(yb, -1.5f), 1.5f);
+            }
+            w = fp4_enc(w, ya, yb, 1.0f, b);
         }
         N[g] = w;
     }
@@ -227,26 +221,13 @@ __device__ __forceinline__ void int3_exact_groups(const float (&v)[32], float s,
 __device__ __forceinline__ Int3Words int3_encode_block(const float (&v)[32])
 {
     const IntScale sc = int_scale<3>(absmax32(v));
-    const float rs2 = sc.zero ? 0.0f : 0.5f * __builtin_amdgcn_rcpf(sc.s);   // ~1/(2s)
-    const float s2 = sc.s + sc.s;
-    const float hs = sc.zero ? __builtin_inff() : 0.5f * sc.s;
-    uint32_t N[4] = {0u, 0u, 0u, 0u};
-    uint32_t redo = sc.abnormal ? 1u : 0u;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float xa = v[8 * b + g], xb = v[8 * b + 4 + g];
-            N[g] = fp4_enc(N[g], xa * rs2, xb * rs2, 1.0f, b);
-            const f2 c = fp4_dec(N[g], 1.0f, b);
-            const float ra = __builtin_fmaf(-c.x, s2, xa), rb = __builtin_fmaf(-c.y, s2, xb);
-            redo |= (uint32_t)(fabsf(ra) >= hs) | (uint32_t)(fabsf(rb) >= hs);
-        }
-    }
+    const float r2 = 0.5f * sc.r;                       // exact
+    uint32_t N[4];
+    int3_groups<false>(v, r2, N);
+    if (sc.abnormal) int3_groups<true>(v, r2, N);
     const uint32_t keep = sc.zero ? 0u : 0xFFFFFFFFu;
 #pragma unroll
     for (int g = 0; g < 4; ++g) N[g] &= keep;
-    if (redo) int3_exact_groups(v, sc.s, sc.zero, N);
     Int3Words o = int3_planes(N);
     o.sbits = sc.zero ? 0u : sc.bits;
     return o;
@@ -279,47 +260,39 @@ __device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32
 
 struct Int4Words { uint32_t d[4]; uint32_t sbits; };
 
-__device__ __forceinline__ void int4_exact_words(const float (&v)[32], float s, bool zero, uint32_t (&D)[4])
+// Sign/magnitude nibbles of x * r9 (r9 = fp32(1/s) * 2^-9) via E4M3
+// subnormal bytes, clamped to +-7 * 2^-9 if CLAMP.
+template <bool CLAMP>
+__device__ __forceinline__ void int4_words(const float (&v)[32], float r9, uint32_t (&D)[4])
 {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        uint32_t w = 0;
+        float y[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float x = v[8 * d + j];
-            uint32_t c = (signbit_u(x) << 3) | int_mag_exact<7>(fabsf(x), s);
-            w |= (zero ? 0u : c) << (4 * j);
+            y[j] = v[8 * d + j] * r9;
+            if (CLAMP) y[j] = fminf(fmaxf(y[j], -7.0f * 0x1p-9f), 7.0f * 0x1p-9f);
         }
-        D[d] = w;
+        // even elements 0,2,4,6 -> bytes of xe; odd 1,3,5,7 -> bytes of xo
+        uint32_t xe = fp8_pair(y[0], y[2], 0u, false);
+        xe = fp8_pair(y[4], y[6], xe, true);
+        uint32_t xo = fp8_pair(y[1], y[3], 0u, false);
+        xo = fp8_pair(y[5], y[7], xo, true);
+        D[d] = (xe & 0x07070707u) | ((xe >> 4) & 0x08080808u) | ((xo << 4) & 0x70707070u) |
+               (xo & 0x80808080u);
     }
 }
 
 __device__ __forceinline__ Int4Words int4_encode_block(const float (&v)[32])
 {
     const IntScale sc = int_scale<7>(absmax32(v));
-    const float rs9 = sc.zero ? 0.0f : __builtin_amdgcn_rcpf(sc.s) * 0x1p-9f;   // ~2^-9 / s
-    const float s9 = sc.s * 512.0f;
-    const float hs = sc.zero ? __builtin_inff() : 0.5f * sc.s;
-    uint32_t redo = sc.abnormal ? 1u : 0u;
+    const float r9 = sc.r * 0x1p-9f;                    // exact
     Int4Words o;
+    int4_words<false>(v, r9, o.d);
+    if (sc.abnormal) int4_words<true>(v, r9, o.d);
+    const uint32_t keep = sc.zero ? 0u : 0xFFFFFFFFu;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const float* x = v + 8 * d;
-        // even elements 0,2,4,6 -> bytes of xe; odd 1,3,5,7 -> bytes of xo
-        uint32_t xe = fp8_pair(x[0] * rs9, x[2] * rs9, 0u, false);
-        xe = fp8_pair(x[4] * rs9, x[6] * rs9, xe, true);
-        uint32_t xo = fp8_pair(x[1] * rs9, x[3] * rs9, 0u, false);
-        xo = fp8_pair(x[5] * rs9, x[7] * rs9, xo, true);
-        const f2 e01 = fp8_dec(xe, false), e23 = fp8_dec(xe, true);
-        const f2 o01 = fp8_dec(xo, false), o23 = fp8_dec(xo, true);
-        const float cs[8] = {e01.x, o01.x, e01.y, o01.y, e23.x, o23.x, e23.y, o23.y};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) redo |= (uint32_t)(fabsf(__builtin_fmaf(-cs[j], s9, x[j])) >= hs);
-        o.d[d] = (xe & 0x07070707u) | ((xe >> 4) & 0x08080808u) | ((xo << 4) & 0x70707070u) |
-                 (xo & 0x80808080u);
-        if (sc.zero) o.d[d] = 0u;
-    }
-    if (redo) int4_exact_words(v, sc.s, sc.zero, o.d);
+    for (int d = 0; d < 4; ++d) o.d[d] &= keep;
     o.sbits = sc.zero ? 0u : sc.bits;
     return o;
 }

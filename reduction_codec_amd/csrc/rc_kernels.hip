@@ -93,6 +93,28 @@ __device__ __forceinline__ void accumulate(const LaneCodes<FMT>& c, float (&acc)
 }
 
 // ------------------------------------------------------------ kernels ----
+//
+// Global memory is touched only by wave-coalesced 16-byte accesses: a tile
+// (or a stream's tile) is read as consecutive 16-byte chunks, chunk c by lane
+// c % 64, with non-temporal hints, and staged through LDS so that each lane
+// then reads its own block.  Unpack output goes the other way.
+
+// Chunk handled by `lane` in load round r of a span of nch 16-byte chunks.
+// Lanes past the end repeat the last chunk (an in-bounds duplicate: same
+// cache line, same LDS bytes), which keeps every load and LDS write
+// unconditional.
+__device__ __forceinline__ int chunk_of(int r, int lane, int nch)
+{
+    const int c = 64 * r + lane;
+    return c < nch ? c : nch - 1;
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ void tail_zero(float (&acc)[32], size_t base, size_t n)
 {
@@ -109,33 +131,110 @@ __device__ __forceinline__ void store_sums_tail(float* __restrict__ sum_out, siz
         if (base + e < n) sum_out[base + e] = acc[e];
 }
 
+template <int DT>
+__device__ __forceinline__ void widen_row(const uint8_t* row, float (&v)[32])
+{
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const u32x4 u = *reinterpret_cast<const u32x4*>(row + 16 * i);
+            v[4 * i] = __uint_as_float(u.x); v[4 * i + 1] = __uint_as_float(u.y);
+            v[4 * i + 2] = __uint_as_float(u.z); v[4 * i + 3] = __uint_as_float(u.w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) widen8<DT>(*reinterpret_cast<const u32x4*>(row + 16 * i), v + 8 * i);
+    }
+}
+
+// R rounds of wave-coalesced 16-byte non-temporal loads of a span of nch
+// chunks starting at p (chunk_of() keeps every lane in bounds).
+template <int R>
+__device__ __forceinline__ void load_chunks(const uint8_t* __restrict__ p, int lane, int nch, u32x4 (&c)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        c[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + chunk_of(r, lane, nch));
+}
+
+template <int R>
+__device__ __forceinline__ void stage_chunks(uint8_t* lds, int lane, int nch, const u32x4 (&c)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(lds + 16 * chunk_of(r, lane, nch)) = c[r];
+}
+
+// Persistent tile loop: each wave walks tiles first, first + stride, ... and
+// loads the next tile's data while it processes the current one.  `first`
+// and `stride` are wave-uniform (scalar registers).
+struct TileWalk {
+    size_t first, stride;
+    int lane, w;
+};
+
+__device__ __forceinline__ TileWalk tile_walk()
+{
+    TileWalk t;
+    t.w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    t.lane = lane_id();
+    t.first = (size_t)blockIdx.x * kWavesPerGroup + (size_t)t.w;
+    t.stride = (size_t)gridDim.x * kWavesPerGroup;
+    return t;
+}
+
 template <int FMT, int DT>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ in, size_t n,
                                                        uint8_t* __restrict__ out, size_t tiles)
 {
-    const size_t tile = tile_index();
-    if (tile >= tiles) return;
-    const int lane = lane_id();
-    float v[32];
-    load_block<DT>(in, tile * kTile + (size_t)lane * kBlock, n, v);
-    encode_store<FMT>(v, out + tile * TileBytes<FMT>::v, lane);
+    constexpr int ES = (DT == kF32) ? 4 : 2;
+    constexpr int TIB = kTile * ES;            // input bytes of one tile
+    constexpr int BB = kBlock * ES;            // input bytes of one block
+    constexpr int ROW = BB + 16;               // padded LDS row: conflict-free 16-byte reads
+    constexpr int CPB = BB / 16;               // chunks per block = load rounds per lane
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    const TileWalk tw = tile_walk();
+    const int lane = tw.lane;
+    const uint8_t* src = static_cast<const uint8_t*>(in);
+    const size_t full = (n % kTile) ? tiles - 1 : tiles;          // tiles without a tail
+    size_t tile = tw.first;
+    if (tile < full) {
+        u32x4 cur[CPB];
+        load_chunks<CPB>(src + tile * TIB, lane, 64 * CPB, cur);
+        for (;;) {
+            const size_t next = tile + tw.stride;
+            const bool more = next < full;
+            u32x4 nxt[CPB];
+            if (more) load_chunks<CPB>(src + next * TIB, lane, 64 * CPB, nxt);
+            wave_lds_sync();                       // previous tile's rows fully read
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) {
+                const int ch = 64 * i + lane;
+                *reinterpret_cast<u32x4*>(&sm[tw.w][(ch / CPB) * ROW + (ch % CPB) * 16]) = cur[i];
+            }
+            wave_lds_sync();
+            float v[32];
+            widen_row<DT>(&sm[tw.w][lane * ROW], v);
+            encode_store<FMT>(v, out + tile * TileBytes<FMT>::v, lane);
+            if (!more) break;
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) cur[i] = nxt[i];
+            tile = next;
+        }
+    }
+    if (full != tiles && (tiles - 1) % tw.stride == tw.first) {   // the partial last tile
+        float v[32];
+        load_block<DT>(in, (tiles - 1) * kTile + (size_t)lane * kBlock, n, v);
+        encode_store<FMT>(v, out + (tiles - 1) * TileBytes<FMT>::v, lane);
+    }
 }
 
-template <int FMT, int K>
-__global__ __launch_bounds__(256) void reduce_kernel(StreamPtrs ins, size_t n, uint8_t* __restrict__ out,
-                                                     float* __restrict__ sum_out, size_t tiles)
+template <int FMT> struct ReduceBatch { static constexpr int v = (FMT == kInt3) ? 8 : 4; };
+
+// Sums of one tile -> optional FP32 sums, tail zeroing, requantized tile.
+template <int FMT>
+__device__ __forceinline__ void reduce_finish(float (&acc)[32], size_t tile, size_t tiles, size_t n, int lane,
+                                              uint8_t* __restrict__ out, float* __restrict__ sum_out)
 {
-    const size_t tile = tile_index();
-    if (tile >= tiles) return;
-    const int lane = lane_id();
-    const size_t off = tile * TileBytes<FMT>::v;
-    LaneCodes<FMT> c[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) c[k] = load_codes<FMT>(ins.p[k] + off, lane);
-    float acc[32];
-    accumulate<FMT, true>(c[0], acc);
-#pragma unroll
-    for (int k = 1; k < K; ++k) accumulate<FMT, false>(c[k], acc);
     const size_t base = tile * kTile + (size_t)lane * kBlock;
     if (tile == tiles - 1 && (n % kTile) != 0) {   // wave-uniform: only the last tile
         tail_zero(acc, base, n);                   // positions >= n are +0
@@ -145,7 +244,77 @@ __global__ __launch_bounds__(256) void reduce_kernel(StreamPtrs ins, size_t n, u
 #pragma unroll
         for (int i = 0; i < 8; ++i) p[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
     }
-    encode_store<FMT>(acc, out + off, lane);
+    encode_store<FMT>(acc, out + tile * TileBytes<FMT>::v, lane);
+}
+
+template <int FMT, int K>
+__global__ __launch_bounds__(256) void reduce_kernel(StreamPtrs ins, size_t n, uint8_t* __restrict__ out,
+                                                     float* __restrict__ sum_out, size_t tiles)
+{
+    constexpr int TB = TileBytes<FMT>::v;
+    constexpr int NCH = TB / 16;               // 16-byte chunks per tile
+    constexpr int RND = (NCH + 63) / 64;
+    constexpr bool PREFETCH = K * RND <= 8;    // whole next tile held in registers
+    constexpr int B = PREFETCH ? K : ((K < ReduceBatch<FMT>::v) ? K : ReduceBatch<FMT>::v);
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][B * TB];
+    const TileWalk tw = tile_walk();
+    const int lane = tw.lane;
+    uint8_t* lds = sm[tw.w];
+    size_t tile = tw.first;
+    if (tile >= tiles) return;
+    if constexpr (PREFETCH) {
+        u32x4 cur[K][RND];
+#pragma unroll
+        for (int k = 0; k < K; ++k) load_chunks<RND>(ins.p[k] + tile * TB, lane, NCH, cur[k]);
+        for (;;) {
+            const size_t next = tile + tw.stride;
+            const bool more = next < tiles;
+            u32x4 nxt[K][RND];
+            if (more) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) load_chunks<RND>(ins.p[k] + next * TB, lane, NCH, nxt[k]);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int k = 0; k < K; ++k) stage_chunks<RND>(lds + k * TB, lane, NCH, cur[k]);
+            wave_lds_sync();
+            float acc[32];
+            accumulate<FMT, true>(load_codes<FMT>(lds, lane), acc);
+#pragma unroll
+            for (int k = 1; k < K; ++k) accumulate<FMT, false>(load_codes<FMT>(lds + k * TB, lane), acc);
+            reduce_finish<FMT>(acc, tile, tiles, n, lane, out, sum_out);
+            if (!more) break;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int r = 0; r < RND; ++r) cur[k][r] = nxt[k][r];
+            tile = next;
+        }
+    } else {
+        for (; tile < tiles; tile += tw.stride) {
+            float acc[32];
+#pragma unroll
+            for (int k0 = 0; k0 < K; k0 += B) {
+                u32x4 c[B][RND];
+#pragma unroll
+                for (int j = 0; j < B; ++j)
+                    if (k0 + j < K) load_chunks<RND>(ins.p[k0 + j] + tile * TB, lane, NCH, c[j]);
+                wave_lds_sync();
+#pragma unroll
+                for (int j = 0; j < B; ++j)
+                    if (k0 + j < K) stage_chunks<RND>(lds + j * TB, lane, NCH, c[j]);
+                wave_lds_sync();
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    if (k0 + j >= K) break;
+                    const LaneCodes<FMT> lc = load_codes<FMT>(lds + j * TB, lane);
+                    if (k0 + j == 0) accumulate<FMT, true>(lc, acc);
+                    else accumulate<FMT, false>(lc, acc);
+                }
+            }
+            reduce_finish<FMT>(acc, tile, tiles, n, lane, out, sum_out);
+        }
+    }
 }
 
 // binary32 -> binary16 bits, RNE.  The empty asm pins x in a register so the
@@ -157,38 +326,34 @@ __device__ __forceinline__ uint32_t f16_bits(float x)
     return __half_as_ushort(__float2half_rn(x));
 }
 
+// The 32 decoded values of one block as output words (16 for 2-byte dtypes).
 template <int ODT>
-__device__ __forceinline__ void store_block(void* __restrict__ out, size_t base, size_t n, const float (&d)[32])
+__device__ __forceinline__ void out_words(const float (&d)[32], uint32_t (&w)[32])
 {
-    if (base + kBlock <= n) {
-        if constexpr (ODT == kF32) {
-            float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + base);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) p[i] = make_float4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
-        } else {
-            uint32_t w[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if constexpr (ODT == kBF16) {
-                    __hip_bfloat162 b = __float22bfloat162_rn(make_float2(d[2 * i], d[2 * i + 1]));
-                    w[i] = *reinterpret_cast<uint32_t*>(&b);
-                } else {
-                    w[i] = f16_bits(d[2 * i]) | (f16_bits(d[2 * i + 1]) << 16);
-                }
+    for (int i = 0; i < 32; ++i) {
+        if constexpr (ODT == kF32) w[i] = __float_as_uint(d[i]);
+        else if (i < 16) {
+            if constexpr (ODT == kBF16) {
+                __hip_bfloat162 b = __float22bfloat162_rn(make_float2(d[2 * i], d[2 * i + 1]));
+                w[i] = *reinterpret_cast<uint32_t*>(&b);
+            } else {
+                w[i] = f16_bits(d[2 * i]) | (f16_bits(d[2 * i + 1]) << 16);
             }
-            uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + base);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
         }
-    } else {
+    }
+}
+
+template <int ODT>
+__device__ __forceinline__ void store_block_guarded(void* __restrict__ out, size_t base, size_t n, const float (&d)[32])
+{
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            if (base + e >= n) continue;
-            if constexpr (ODT == kF32) static_cast<float*>(out)[base + e] = d[e];
-            else if constexpr (ODT == kBF16)
-                static_cast<uint16_t*>(out)[base + e] = __bfloat16_as_ushort(__float2bfloat16(d[e]));
-            else static_cast<uint16_t*>(out)[base + e] = (uint16_t)f16_bits(d[e]);
-        }
+    for (int e = 0; e < 32; ++e) {
+        if (base + e >= n) continue;
+        if constexpr (ODT == kF32) static_cast<float*>(out)[base + e] = d[e];
+        else if constexpr (ODT == kBF16)
+            static_cast<uint16_t*>(out)[base + e] = __bfloat16_as_ushort(__float2bfloat16(d[e]));
+        else static_cast<uint16_t*>(out)[base + e] = (uint16_t)f16_bits(d[e]);
     }
 }
 
@@ -196,29 +361,79 @@ template <int FMT, int ODT>
 __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ in, size_t n,
                                                      void* __restrict__ out, size_t tiles)
 {
-    const size_t tile = tile_index();
+    constexpr int TB = TileBytes<FMT>::v;
+    constexpr int NCH = TB / 16;
+    constexpr int RND = (NCH + 63) / 64;
+    constexpr int ES = (ODT == kF32) ? 4 : 2;
+    constexpr int OB = kBlock * ES;            // output bytes of one block
+    constexpr int ROW = OB + 16;
+    constexpr int CPB = OB / 16;
+    __shared__ __attribute__((aligned(16))) uint8_t smi[kWavesPerGroup][TB];
+    __shared__ __attribute__((aligned(16))) uint8_t smo[kWavesPerGroup][64 * ROW];
+    const TileWalk tw = tile_walk();
+    const int lane = tw.lane;
+    size_t tile = tw.first;
     if (tile >= tiles) return;
-    const int lane = lane_id();
-    const LaneCodes<FMT> c = load_codes<FMT>(in + tile * TileBytes<FMT>::v, lane);
-    float d[32];
-    accumulate<FMT, true>(c, d);
-    store_block<ODT>(out, tile * kTile + (size_t)lane * kBlock, n, d);
+    u32x4 cur[RND];
+    load_chunks<RND>(in + tile * TB, lane, NCH, cur);
+    for (;;) {
+        const size_t next = tile + tw.stride;
+        const bool more = next < tiles;
+        u32x4 nxt[RND];
+        if (more) load_chunks<RND>(in + next * TB, lane, NCH, nxt);
+        wave_lds_sync();
+        stage_chunks<RND>(smi[tw.w], lane, NCH, cur);
+        wave_lds_sync();
+        float d[32];
+        accumulate<FMT, true>(load_codes<FMT>(smi[tw.w], lane), d);
+        const size_t base = tile * kTile + (size_t)lane * kBlock;
+        if (tile == tiles - 1 && (n % kTile) != 0) {
+            store_block_guarded<ODT>(out, base, n, d);
+        } else {
+            uint32_t wd[32];
+            out_words<ODT>(d, wd);
+#pragma unroll
+            for (int i = 0; i < CPB; ++i)
+                *reinterpret_cast<u32x4*>(&smo[tw.w][lane * ROW + 16 * i]) =
+                    (u32x4){wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]};
+            wave_lds_sync();
+            u32x4* q = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(out) + tile * (size_t)(kTile * ES));
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) {
+                const int ch = 64 * i + lane;
+                q[ch] = *reinterpret_cast<const u32x4*>(&smo[tw.w][(ch / CPB) * ROW + (ch % CPB) * 16]);
+            }
+        }
+        if (!more) break;
+#pragma unroll
+        for (int r = 0; r < RND; ++r) cur[r] = nxt[r];
+        tile = next;
+    }
 }
 
-__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ in, uint4* __restrict__ out, size_t n16)
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out, size_t n16)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = in[i], b = in[i + stride], c = in[i + 2 * stride], d = in[i + 3 * stride];
-        out[i] = a; out[i + stride] = b; out[i + 2 * stride] = c; out[i + 3 * stride] = d;
-    }
-    for (; i < n16; i += stride) out[i] = in[i];
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(in + i), out + i);
 }
 
 // ---------------------------------------------------------- launchers ----
 
-static inline dim3 tile_grid(size_t tiles) { return dim3((unsigned)((tiles + kWavesPerGroup - 1) / kWavesPerGroup)); }
+#ifndef RC_GROUPS_PER_CU
+#define RC_GROUPS_PER_CU 8
+#endif
+
+// Persistent grid: at most RC_GROUPS_PER_CU four-wave workgroups per compute
+// unit, fewer when there are fewer tiles.
+static inline dim3 tile_grid(size_t tiles)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const size_t groups = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+    const size_t cap = (size_t)RC_GROUPS_PER_CU * (size_t)(cus > 0 ? cus : 256);
+    return dim3((unsigned)(groups < cap ? groups : cap));
+}
 
 template <int FMT>
 static hipError_t launch_quantize_fmt(int dt, const void* in, size_t n, void* out, size_t tiles, hipStream_t st)
@@ -312,11 +527,11 @@ hipError_t launch_unpack(int fmt, const void* in, size_t n, int dt, void* out, h
 hipError_t launch_copy(const void* in, void* out, size_t bytes, hipStream_t st)
 {
     const size_t n16 = bytes / 16;
-    size_t blocks = (n16 + 4 * 256 - 1) / (4 * 256);
-    if (blocks > 65536) blocks = 65536;
+    size_t blocks = (n16 + 255) / 256;         // one 16-byte chunk per thread
+    if (blocks > (1u << 20)) blocks = 1u << 20;
     if (blocks == 0) blocks = 1;
-    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint4*>(in),
-                       static_cast<uint4*>(out), n16);
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const u32x4*>(in),
+                       static_cast<u32x4*>(out), n16);
     return hipGetLastError();
 }
 
