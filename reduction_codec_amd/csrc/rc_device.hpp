@@ -15,10 +15,11 @@
 //   * INT4 magnitudes 0..7 are the E4M3 subnormals m * 2^-9, so a sign /
 //     magnitude INT4 code is an E4M3 byte with exponent 0.
 // Both conversions round their binary32 input to nearest even, which is the
-// INT rounding rule itself: magnitude = RNE(fp32(|x| * fp32(1/s))).  For a
-// normal, unsaturated fp16 scale |x| * r <= qmax + 0.004, so no clamp is
-// needed; blocks with a subnormal or saturated scale are re-encoded with a
-// clamp behind a (rarely taken) branch.
+// INT rounding rule itself: magnitude = min(RNE(fp32(|x| * fp32(1/s))), qmax).
+// Below the clamp the code's low bit is the parity of the integer, so ties
+// go the same way.  For a normal, unsaturated fp16 scale |x| * r <= qmax +
+// 0.004, so no clamp is needed; for a subnormal or saturated scale the clamp
+// is applied to the packed codes (every code above qmax becomes qmax).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -153,20 +154,41 @@ struct IntScale {
     bool abnormal;    // subnormal fp16 or saturated: codes need the clamp
 };
 
-// s = fp16(min(fp32(a / qmax), 65504)); fp32 division is the IEEE one.
+// Correctly rounded a / b for a constant b: q = a * RN(1/b), then one
+// residual correction.  For b = 3, 7 and 448 this equals the IEEE quotient
+// for every finite a >= 0 (448: wherever the quotient is normal), which an
+// exhaustive run over all binary32 inputs confirms; an infinite a gives NaN.
+template <int B>
+__device__ __forceinline__ float div_by(float a)
+{
+    constexpr float y = 1.0f / (float)B;
+    const float q = a * y;
+    return __builtin_fmaf(__builtin_fmaf(-q, (float)B, a), y, q);
+}
+
+// RN(1/s) for a positive fp16 scale s (as binary32): the hardware
+// reciprocal (within 1 ulp) plus one Newton step, which is correctly rounded
+// for every fp16 value and every starting point within 1 ulp.
+__device__ __forceinline__ float recip_f16_scale(float s)
+{
+    const float y0 = __builtin_amdgcn_rcpf(s);
+    return __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
+}
+
+// s = fp16(min(fp32(a / qmax), 65504)) with the IEEE binary32 quotient.
 template <int QMAX>
 __device__ __forceinline__ IntScale int_scale(float a)
 {
     IntScale r;
-    float s32 = a / (float)QMAX;
-    bool sat = s32 > 65504.0f;
+    float s32 = div_by<QMAX>(a);
+    const bool sat = !(s32 <= 65504.0f);            // also an infinite a (NaN quotient)
     s32 = fminf(s32, 65504.0f);
     __half h = __float2half_rn(s32);
     r.bits = __half_as_ushort(h);
     r.s = __half2float(h);
     r.zero = (r.s == 0.0f);
     r.abnormal = sat || (!r.zero && r.s < 0x1p-14f);
-    r.r = r.zero ? 0.0f : 1.0f / r.s;
+    r.r = r.zero ? 0.0f : recip_f16_scale(r.s);
     return r;
 }
 
@@ -198,24 +220,24 @@ __device__ __forceinline__ uint32_t int3_group(uint32_t w0, uint32_t w1, uint32_
 }
 
 // E2M1 nibbles of the 32 elements, group g in word N[g] (nibble j = element
-// 4j + g), of x * r2 with r2 = fp32(1/s) / 2, clamped to +-1.5 if CLAMP.
-template <bool CLAMP>
+// 4j + g), of x * r2 with r2 = fp32(1/s) / 2.
 __device__ __forceinline__ void int3_groups(const float (&v)[32], float r2, uint32_t (&N)[4])
 {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         uint32_t w = 0u;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            float ya = v[8 * b + g] * r2, yb = v[8 * b + 4 + g] * r2;
-            if (CLAMP) {
-                ya = fminf(fmaxf(ya, -1.5f), 1.5f);
-                yb = fminf(fmaxf(yb, -1.5f), 1.5f);
-            }
-            w = fp4_enc(w, ya, yb, 1.0f, b);
-        }
+        for (int b = 0; b < 4; ++b) w = fp4_enc(w, v[8 * b + g] * r2, v[8 * b + 4 + g] * r2, 1.0f, b);
         N[g] = w;
     }
+}
+
+// min(magnitude, 3) on E2M1 nibbles: a magnitude code with bit 2 set (an E2M1
+// value of 2 or more, i.e. an INT3 magnitude of 4 or more) becomes 3.
+__device__ __forceinline__ uint32_t int3_clamp_word(uint32_t w)
+{
+    const uint32_t big = (w >> 2) & 0x11111111u;
+    return (w & 0x88888888u) | (w & 0x33333333u) | (big * 3u);
 }
 
 __device__ __forceinline__ Int3Words int3_encode_block(const float (&v)[32])
@@ -223,8 +245,12 @@ __device__ __forceinline__ Int3Words int3_encode_block(const float (&v)[32])
     const IntScale sc = int_scale<3>(absmax32(v));
     const float r2 = 0.5f * sc.r;                       // exact
     uint32_t N[4];
-    int3_groups<false>(v, r2, N);
-    if (sc.abnormal) int3_groups<true>(v, r2, N);
+    int3_groups(v, r2, N);
+    // Only a subnormal or saturated scale lets |x| * r exceed 3 + 1/2.
+    if (sc.abnormal) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) N[g] = int3_clamp_word(N[g]);
+    }
     const uint32_t keep = sc.zero ? 0u : 0xFFFFFFFFu;
 #pragma unroll
     for (int g = 0; g < 4; ++g) N[g] &= keep;
@@ -260,39 +286,39 @@ __device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32
 
 struct Int4Words { uint32_t d[4]; uint32_t sbits; };
 
-// Sign/magnitude nibbles of x * r9 (r9 = fp32(1/s) * 2^-9) via E4M3
-// subnormal bytes, clamped to +-7 * 2^-9 if CLAMP.
-template <bool CLAMP>
-__device__ __forceinline__ void int4_words(const float (&v)[32], float r9, uint32_t (&D)[4])
+// min(magnitude, 7) on four E4M3 bytes of INT4 codes: a byte with a nonzero
+// exponent field (value 8 * 2^-9 or more) gets mantissa bits 111; only the
+// mantissa and sign bits are packed afterwards.
+__device__ __forceinline__ uint32_t int4_clamp_bytes(uint32_t x)
 {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        float y[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            y[j] = v[8 * d + j] * r9;
-            if (CLAMP) y[j] = fminf(fmaxf(y[j], -7.0f * 0x1p-9f), 7.0f * 0x1p-9f);
-        }
-        // even elements 0,2,4,6 -> bytes of xe; odd 1,3,5,7 -> bytes of xo
-        uint32_t xe = fp8_pair(y[0], y[2], 0u, false);
-        xe = fp8_pair(y[4], y[6], xe, true);
-        uint32_t xo = fp8_pair(y[1], y[3], 0u, false);
-        xo = fp8_pair(y[5], y[7], xo, true);
-        D[d] = (xe & 0x07070707u) | ((xe >> 4) & 0x08080808u) | ((xo << 4) & 0x70707070u) |
-               (xo & 0x80808080u);
-    }
+    const uint32_t big = (((x & 0x78787878u) + 0x78787878u) >> 7) & 0x01010101u;
+    return x | big | (big << 1) | (big << 2);
 }
 
 __device__ __forceinline__ Int4Words int4_encode_block(const float (&v)[32])
 {
     const IntScale sc = int_scale<7>(absmax32(v));
     const float r9 = sc.r * 0x1p-9f;                    // exact
-    Int4Words o;
-    int4_words<false>(v, r9, o.d);
-    if (sc.abnormal) int4_words<true>(v, r9, o.d);
-    const uint32_t keep = sc.zero ? 0u : 0xFFFFFFFFu;
+    // E4M3 subnormal bytes of x * r9: word d's even elements 0,2,4,6 in the
+    // bytes of xe[d], odd elements 1,3,5,7 in xo[d]
+    uint32_t xe[4], xo[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) o.d[d] &= keep;
+    for (int d = 0; d < 4; ++d) {
+        const float* y = v + 8 * d;
+        xe[d] = fp8_pair(y[4] * r9, y[6] * r9, fp8_pair(y[0] * r9, y[2] * r9, 0u, false), true);
+        xo[d] = fp8_pair(y[5] * r9, y[7] * r9, fp8_pair(y[1] * r9, y[3] * r9, 0u, false), true);
+    }
+    // Only a subnormal or saturated scale lets |x| * r exceed 7 + 1/2.
+    if (sc.abnormal) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) { xe[d] = int4_clamp_bytes(xe[d]); xo[d] = int4_clamp_bytes(xo[d]); }
+    }
+    const uint32_t keep = sc.zero ? 0u : 0xFFFFFFFFu;
+    Int4Words o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        o.d[d] = ((xe[d] & 0x07070707u) | ((xe[d] >> 4) & 0x08080808u) | ((xo[d] << 4) & 0x70707070u) |
+                  (xo[d] & 0x80808080u)) & keep;
     o.sbits = sc.zero ? 0u : sc.bits;
     return o;
 }
@@ -339,7 +365,8 @@ __device__ __forceinline__ float fp8_ro_quotient(float x, float s)
 __device__ __forceinline__ Fp8Words fp8_encode_block(const float (&v)[32])
 {
     Fp8Words o;
-    float s = absmax32(v) / 448.0f;
+    const float a = absmax32(v);
+    const float s = (a == __builtin_inff()) ? a : div_by<448>(a);   // inf / 448 = inf
     const bool zero = !(s >= 0x1p-126f);
     o.s = zero ? 0.0f : s;
     const float sd = zero ? 1.0f : s;

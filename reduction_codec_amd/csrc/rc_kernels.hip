@@ -7,6 +7,16 @@
 #include "rc_device.hpp"
 #include "rc_internal.hpp"
 
+#ifndef RC_GROUPS_PER_CU
+#define RC_GROUPS_PER_CU 64                        // grid cap, workgroups per CU
+#endif
+#ifndef RC_REDUCE_WAVES
+#define RC_REDUCE_WAVES 8                          // reduce occupancy target (waves per SIMD), INT / MX
+#endif
+#ifndef RC_REDUCE_BATCH
+#define RC_REDUCE_BATCH 2                          // streams loaded together, INT / MX
+#endif
+
 namespace rc {
 
 template <int FMT> struct TileBytes;
@@ -73,6 +83,76 @@ __device__ __forceinline__ LaneCodes<FMT> load_codes(const uint8_t* __restrict__
         c.e8 = t[1024 + lane];
     }
     return c;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------ buffer access ----
+// Tiles are addressed through a buffer descriptor built in scalar registers
+// from the (wave-uniform) tile address, and a per-lane byte offset that
+// does not change from tile to tile: no per-lane 64-bit address arithmetic.
+// Loads and stores carry the non-temporal hint.
+
+constexpr int kNT = 2;                              // aux bits: nt
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc span_rsrc(const void* base, size_t off, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const uint8_t*>(base) + off), (short)0,
+                                             (int)bytes, 0x00020000);
+}
+
+// The per-lane code words of one block, read from a stream's tile.
+template <int FMT>
+__device__ __forceinline__ LaneCodes<FMT> load_codes_buf(Rsrc r, uint32_t lane)
+{
+    LaneCodes<FMT> c;
+    if constexpr (FMT == kInt3) {
+        const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8u, 0, kNT);
+        c.q2 = make_uint2(q.x, q.y);
+        c.h = __builtin_amdgcn_raw_buffer_load_b32(r, 512u + lane * 4u, 0, kNT);
+        c.s = __builtin_amdgcn_raw_buffer_load_b16(r, 768u + lane * 2u, 0, kNT);
+    } else if constexpr (FMT == kInt4) {
+        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, kNT);
+        c.d = make_uint4(d.x, d.y, d.z, d.w);
+        c.s = __builtin_amdgcn_raw_buffer_load_b16(r, 1024u + lane * 2u, 0, kNT);
+    } else if constexpr (FMT == kFp8) {
+        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 32u, 0, kNT);
+        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 32u + 16u, 0, kNT);
+        c.d0 = make_uint4(d0.x, d0.y, d0.z, d0.w);
+        c.d1 = make_uint4(d1.x, d1.y, d1.z, d1.w);
+        c.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 2048u + lane * 4u, 0, kNT));
+    } else {
+        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, kNT);
+        c.d = make_uint4(d.x, d.y, d.z, d.w);
+        c.e8 = __builtin_amdgcn_raw_buffer_load_b8(r, 1024u + lane, 0, kNT);
+    }
+    return c;
+}
+
+// Requantize the 32 values of lane's block and store its code words.
+template <int FMT>
+__device__ __forceinline__ void encode_store_buf(const float (&v)[32], Rsrc r, uint32_t lane)
+{
+    if constexpr (FMT == kInt3) {
+        const Int3Words w = int3_encode_block(v);
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){w.w0, w.w1}, r, lane * 8u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b32(w.h, r, 512u + lane * 4u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w.sbits, r, 768u + lane * 2u, 0, kNT);
+    } else if constexpr (FMT == kInt4) {
+        const Int4Words w = int4_encode_block(v);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){w.d[0], w.d[1], w.d[2], w.d[3]}, r, lane * 16u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w.sbits, r, 1024u + lane * 2u, 0, kNT);
+    } else if constexpr (FMT == kFp8) {
+        const Fp8Words w = fp8_encode_block(v);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){w.d[0], w.d[1], w.d[2], w.d[3]}, r, lane * 32u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){w.d[4], w.d[5], w.d[6], w.d[7]}, r, lane * 32u + 16u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(w.s), r, 2048u + lane * 4u, 0, kNT);
+    } else {
+        const MxWords w = mx_encode_block(v);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){w.d[0], w.d[1], w.d[2], w.d[3]}, r, lane * 16u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)w.e8, r, 1024u + lane, 0, kNT);
+    }
 }
 
 template <int FMT, bool FIRST>
@@ -228,92 +308,81 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     }
 }
 
-template <int FMT> struct ReduceBatch { static constexpr int v = (FMT == kInt3) ? 8 : 4; };
+// Streams whose codes are loaded together before they are accumulated.
+// FP8's encoder holds more registers: it runs at 6 waves per SIMD (80 VGPRs).
+template <int FMT> struct ReduceBatch { static constexpr int v = (FMT == kFp8) ? 2 : RC_REDUCE_BATCH; };
+template <int FMT> struct ReduceWaves { static constexpr int v = (FMT == kFp8) ? 6 : RC_REDUCE_WAVES; };
 
-// Sums of one tile -> optional FP32 sums, tail zeroing, requantized tile.
-template <int FMT>
-__device__ __forceinline__ void reduce_finish(float (&acc)[32], size_t tile, size_t tiles, size_t n, int lane,
-                                              uint8_t* __restrict__ out, float* __restrict__ sum_out)
-{
-    const size_t base = tile * kTile + (size_t)lane * kBlock;
-    if (tile == tiles - 1 && (n % kTile) != 0) {   // wave-uniform: only the last tile
-        tail_zero(acc, base, n);                   // positions >= n are +0
-        if (sum_out) store_sums_tail(sum_out, base, n, acc);
-    } else if (sum_out) {
-        float4* p = reinterpret_cast<float4*>(sum_out + base);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
-    }
-    encode_store<FMT>(acc, out + tile * TileBytes<FMT>::v, lane);
-}
-
+// acc = the K streams' decoded values of lane's block of `tile`, added in
+// stream order in binary32.
 template <int FMT, int K>
-__global__ __launch_bounds__(256) void reduce_kernel(StreamPtrs ins, size_t n, uint8_t* __restrict__ out,
-                                                     float* __restrict__ sum_out, size_t tiles)
+__device__ __forceinline__ void reduce_tile(const StreamPtrs& ins, size_t tile, uint32_t lane, float (&acc)[32])
 {
     constexpr int TB = TileBytes<FMT>::v;
-    constexpr int NCH = TB / 16;               // 16-byte chunks per tile
-    constexpr int RND = (NCH + 63) / 64;
-    constexpr bool PREFETCH = K * RND <= 8;    // whole next tile held in registers
-    constexpr int B = PREFETCH ? K : ((K < ReduceBatch<FMT>::v) ? K : ReduceBatch<FMT>::v);
-    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][B * TB];
+    constexpr int B = (K < ReduceBatch<FMT>::v) ? K : ReduceBatch<FMT>::v;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += B) {
+        LaneCodes<FMT> c[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (k0 + j < K) c[j] = load_codes_buf<FMT>(span_rsrc(ins.p[k0 + j], tile * TB, TB), lane);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (k0 + j >= K) break;
+            if (k0 + j == 0) accumulate<FMT, true>(c[j], acc);
+            else accumulate<FMT, false>(c[j], acc);
+        }
+        // keep the next batch's loads below this batch's arithmetic (bounds
+        // the registers held by codes in flight)
+        if (k0 + B < K) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__device__ __forceinline__ void store_sums(float* __restrict__ sum_out, size_t tile, uint32_t lane, const float (&acc)[32])
+{
+    const Rsrc r = span_rsrc(sum_out, tile * (kTile * 4), kTile * 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){__float_as_uint(acc[4 * i]), __float_as_uint(acc[4 * i + 1]),
+                                                       __float_as_uint(acc[4 * i + 2]), __float_as_uint(acc[4 * i + 3])},
+                                               r, lane * 128u + 16u * i, 0, kNT);
+}
+
+// Each wave reduces whole tiles: the codes of the K streams are read with
+// per-lane coalesced loads (ReduceBatch streams at a time), decoded and
+// accumulated in registers, and the sums requantized in place.  No LDS and
+// no in-wave prefetch: latency is covered by the other waves of the SIMD.
+// The partial last tile (if any) is done after the loop by the wave whose
+// walk would reach it.
+template <int FMT, int K>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ReduceWaves<FMT>::v)))
+void reduce_kernel(StreamPtrs ins, size_t n, uint8_t* __restrict__ out, float* __restrict__ sum_out, size_t tiles)
+{
+    constexpr int TB = TileBytes<FMT>::v;
     const TileWalk tw = tile_walk();
-    const int lane = tw.lane;
-    uint8_t* lds = sm[tw.w];
-    size_t tile = tw.first;
-    if (tile >= tiles) return;
-    if constexpr (PREFETCH) {
-        u32x4 cur[K][RND];
-#pragma unroll
-        for (int k = 0; k < K; ++k) load_chunks<RND>(ins.p[k] + tile * TB, lane, NCH, cur[k]);
-        for (;;) {
-            const size_t next = tile + tw.stride;
-            const bool more = next < tiles;
-            u32x4 nxt[K][RND];
-            if (more) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) load_chunks<RND>(ins.p[k] + next * TB, lane, NCH, nxt[k]);
-            }
-            wave_lds_sync();
-#pragma unroll
-            for (int k = 0; k < K; ++k) stage_chunks<RND>(lds + k * TB, lane, NCH, cur[k]);
-            wave_lds_sync();
+    const uint32_t lane = (uint32_t)tw.lane;
+    const size_t full = n / kTile;
+    if (sum_out) {
+        for (size_t tile = tw.first; tile < full; tile += tw.stride) {
             float acc[32];
-            accumulate<FMT, true>(load_codes<FMT>(lds, lane), acc);
-#pragma unroll
-            for (int k = 1; k < K; ++k) accumulate<FMT, false>(load_codes<FMT>(lds + k * TB, lane), acc);
-            reduce_finish<FMT>(acc, tile, tiles, n, lane, out, sum_out);
-            if (!more) break;
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-#pragma unroll
-                for (int r = 0; r < RND; ++r) cur[k][r] = nxt[k][r];
-            tile = next;
+            reduce_tile<FMT, K>(ins, tile, lane, acc);
+            store_sums(sum_out, tile, lane, acc);
+            encode_store_buf<FMT>(acc, span_rsrc(out, tile * TB, TB), lane);
         }
     } else {
-        for (; tile < tiles; tile += tw.stride) {
+        for (size_t tile = tw.first; tile < full; tile += tw.stride) {
             float acc[32];
-#pragma unroll
-            for (int k0 = 0; k0 < K; k0 += B) {
-                u32x4 c[B][RND];
-#pragma unroll
-                for (int j = 0; j < B; ++j)
-                    if (k0 + j < K) load_chunks<RND>(ins.p[k0 + j] + tile * TB, lane, NCH, c[j]);
-                wave_lds_sync();
-#pragma unroll
-                for (int j = 0; j < B; ++j)
-                    if (k0 + j < K) stage_chunks<RND>(lds + j * TB, lane, NCH, c[j]);
-                wave_lds_sync();
-#pragma unroll
-                for (int j = 0; j < B; ++j) {
-                    if (k0 + j >= K) break;
-                    const LaneCodes<FMT> lc = load_codes<FMT>(lds + j * TB, lane);
-                    if (k0 + j == 0) accumulate<FMT, true>(lc, acc);
-                    else accumulate<FMT, false>(lc, acc);
-                }
-            }
-            reduce_finish<FMT>(acc, tile, tiles, n, lane, out, sum_out);
+            reduce_tile<FMT, K>(ins, tile, lane, acc);
+            encode_store_buf<FMT>(acc, span_rsrc(out, tile * TB, TB), lane);
         }
+    }
+    if (full != tiles && full % tw.stride == tw.first) {
+        float acc[32];
+        reduce_tile<FMT, K>(ins, full, lane, acc);
+        const size_t base = full * kTile + (size_t)lane * kBlock;
+        tail_zero(acc, base, n);                   // positions >= n are +0
+        if (sum_out) store_sums_tail(sum_out, base, n, acc);
+        encode_store_buf<FMT>(acc, span_rsrc(out, full * TB, TB), lane);
     }
 }
 
@@ -420,12 +489,10 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ in,
 
 // ---------------------------------------------------------- launchers ----
 
-#ifndef RC_GROUPS_PER_CU
-#define RC_GROUPS_PER_CU 8
-#endif
 
-// Persistent grid: at most RC_GROUPS_PER_CU four-wave workgroups per compute
-// unit, fewer when there are fewer tiles.
+// Grid of four-wave workgroups: one tile per wave up to RC_GROUPS_PER_CU
+// workgroups per compute unit (about 1 GiB of bf16 input on 256 CUs);
+// beyond that each wave walks several tiles.
 static inline dim3 tile_grid(size_t tiles)
 {
     int dev = 0, cus = 256;
