@@ -5,15 +5,20 @@ quantize_pack of a 64 MiB bf16 message (33,554,432 Student-t values) into the
 first of four packed stream buffers, then a 4-stream dequant_reduce_requant of
 that stream and three pre-packed peer streams into one packed output.  Inputs
 are resident in HBM before timing starts; eight buffer sets are rotated so the
-working set (about 1 GiB) defeats the 256 MiB Infinity Cache.
+working set (about 1 GiB) defeats the 256 MiB Infinity Cache.  After the
+eager warmup steps, the timed steps are recorded into one HIP graph and
+replayed once, so the timed region holds GPU work only.
 
 Prints one JSON line: value = uncompressed GB/s (input bytes of the quantize
 plus K x message bytes of the reduce, per second), a `roofline` object for the
-dominant kernel (algorithmic bytes per launch / average launch time from HIP
-events, against 8 TB/s) and a `cpu_baseline` object (the plain C oracle on
-the host cores over the same workload).
+dominant kernel (algorithmic bytes per launch / average launch time, from HIP
+events around a graph of back-to-back launches, against 8 TB/s) and a
+`cpu_baseline` object (the plain C oracle on the host cores over a sample of
+the same workload).
 
 Extra modes:
+  --table                               per-kernel table over all formats and
+                                        sizes (--table-mib)
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc` runs of this
                                         script into profiles/traffic_*.json
 """
@@ -54,6 +59,11 @@ def parse_args():
     ap.add_argument("--sets", type=int, default=0, help="rotation buffer sets (0 = enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
+                    help="per-kernel duration table from a rocprofv3 --kernel-trace results database")
+    ap.add_argument("--table", action="store_true",
+                    help="per-kernel table over every format and --table-mib sizes (no JSON line)")
+    ap.add_argument("--table-mib", default="16,64,256,1024")
     return ap.parse_args()
 
 
@@ -104,6 +114,20 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
     print(json.dumps(out))
 
 
+def summarize_trace(db_path: str) -> int:
+    """Markdown table of kernel dispatch durations (count, average, min, max
+    in ns) from the SQLite database rocprofv3 writes with --kernel-trace."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = con.execute("select name, count(*), avg(end - start), min(end - start), max(end - start), "
+                       "sum(end - start) from kernels group by name order by sum(end - start) desc").fetchall()
+    print("| kernel | calls | avg ns | min ns | max ns | total ns |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, cnt, avg, lo, hi, tot in rows:
+        print(f"| {name.split('(')[0]} | {cnt} | {avg:.0f} | {lo} | {hi} | {tot} |")
+    return 0
+
+
 def traffic_for(kernel_key: str):
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -123,6 +147,10 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return 0
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
+    if args.table:
+        return table(args)
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU only: this codec build has no multi-GPU path "
                          "(run with --gpus 1)\n")
@@ -161,29 +189,6 @@ def main():
         rca.quantize_pack(x, codec, out=streams[0])
         rca.dequant_reduce_requant(streams, codec, n, out=out)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # per-kernel launch durations (HIP events on the launch stream)
-    def timed(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i, (a, b) in enumerate(evs):
-            a.record()
-            fn(i)
-            b.record()
-        torch.cuda.synchronize()
-        return sorted(a.elapsed_time(b) for a, b in evs)
-
     def q_only(i):
         x, streams, _ = bufs[i % sets]
         rca.quantize_pack(x, codec, out=streams[0])
@@ -192,16 +197,62 @@ def main():
         _, streams, out = bufs[i % sets]
         rca.dequant_reduce_requant(streams, codec, n, out=out)
 
+    # W eager warmup steps; then the K timed steps are recorded once into a
+    # HIP graph (buffer sets rotating) and replayed, so the timed region holds
+    # GPU work only, without per-call host overhead.  Per-kernel durations come
+    # from graphs of back-to-back launches of one kernel.  Events are recorded
+    # on the replay stream.
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    def capture(fn, count, first=0):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(first, first + count):
+                fn(i)
+        return g
+
+    timed_steps = capture(step, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    timed_steps.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    del timed_steps
+
+    def timed(fn, reps):
+        g = capture(fn, reps)
+        g.replay()                                  # warm
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
     reps = max(20, args.steps)
-    tq = timed(q_only, reps)
-    tr = timed(r_only, reps)
-    q_ms, r_ms = sum(tq) / len(tq), sum(tr) / len(tr)
+    q_ms = timed(q_only, reps)
+    r_ms = timed(r_only, reps)
+
+    # the replayed graphs computed what the eager calls compute
+    capture(step, 1).replay()
+    torch.cuda.synchronize()
+    x, streams, out = bufs[0]
+    q_eager = rca.quantize_pack(x, codec)
+    r_eager, _ = rca.dequant_reduce_requant([q_eager] + streams[1:], codec, n)
+    torch.cuda.synchronize()
+    if not (torch.equal(q_eager, streams[0]) and torch.equal(r_eager, out)):
+        raise RuntimeError("graph replay output differs from the eager launch")
 
     # plain copy of 256 MiB: the achievable-bandwidth reference in this run
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    tc = timed(lambda i: rca.copy(dst, src), 20)
-    c_ms = sum(tc) / len(tc)
+    c_ms = timed(lambda i: rca.copy(dst, src), 20)
     del src, dst
 
     q_bytes = 2 * n + pb                      # algorithmic HBM bytes of one quantize launch
@@ -238,9 +289,78 @@ def main():
             "step_hbm_gbs": round(step_hbm, 1), "step_hbm_frac": round(step_hbm / HBM_PEAK_GBS, 4),
             "copy_256MiB_gbs": round(2 * COPY_BYTES / (c_ms * 1e-3) / 1e9, 1),
             "host_wall_ms_per_step": round(wall_ms, 5),
+            "timing": "HIP graph replays; events on the replay stream",
         },
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def table(args):
+    """Average launch time of every kernel family per format and message size
+    (bf16 messages; K packed streams for the reduce), from a HIP graph of 30
+    back-to-back launches, with algorithmic HBM bytes per launch / time
+    against the 8 TB/s peak."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import reduction_codec_amd as rca
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def timed(fn, reps=30):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()                  # back-to-back launches, no host overhead
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    print("| MiB | format | kernel | us | HBM GB/s | % of peak | uncompressed GB/s |")
+    print("|---:|---|---|---:|---:|---:|---:|")
+    for mib in [int(v) for v in args.table_mib.split(",")]:
+        n = mib * (1 << 20) // 2
+        x0 = torch.from_numpy(datagen.bf16_student4(2 * n, 0).view(np.int16)).view(torch.bfloat16).to(dev)
+        for fmt in ("int3", "int4", "fp8", "mxfp4"):
+            codec = rca.CODECS[fmt]
+            pb = rca.packed_bytes(codec, n)
+            kmax = 8
+            sets = max(1, -(-(1 << 30) // (4 * n + (kmax + 1) * pb)))
+            bufs = []
+            for _ in range(sets):
+                x = x0.clone()
+                p = rca.quantize_pack(x, codec)
+                streams = [p] + [p.clone() for _ in range(kmax - 1)]
+                bufs.append((x, streams, torch.empty(pb, dtype=torch.uint8, device=dev),
+                             torch.empty(n, dtype=torch.bfloat16, device=dev)))
+            torch.cuda.synchronize()
+            rows = [("quantize_pack bf16", lambda i: rca.quantize_pack(bufs[i % sets][0], codec, out=bufs[i % sets][2]),
+                     2 * n + pb, 2 * n)]
+            for K in (2, 4, 8):
+                rows.append((f"dequant_reduce_requant K={K}",
+                             (lambda K: lambda i: rca.dequant_reduce_requant(bufs[i % sets][1][:K], codec, n,
+                                                                              out=bufs[i % sets][2]))(K),
+                             (K + 1) * pb, K * 2 * n))
+            rows.append(("unpack_dequant bf16",
+                         lambda i: rca.unpack_dequant(bufs[i % sets][2], codec, n, torch.bfloat16, out=bufs[i % sets][3]),
+                         pb + 2 * n, 2 * n))
+            for name, fn, hbm, unc in rows:
+                ms = timed(fn)
+                g = hbm / (ms * 1e-3) / 1e9
+                print(f"| {mib} | {fmt} | {name} | {ms * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
+                      f"{unc / (ms * 1e-3) / 1e9:.0f} |", flush=True)
+            del bufs
+            torch.cuda.empty_cache()
     return 0
 
 
