@@ -347,19 +347,37 @@ __device__ __forceinline__ void int4_accumulate(const uint32_t (&D)[4], uint32_t
 
 struct Fp8Words { uint32_t d[8]; float s; };
 
-// E4M3 code (with sign) of the exact quotient x / s: the IEEE binary32
-// quotient and its exact residual give the round-to-odd binary32 value of the
-// quotient, whose round-to-nearest-even E4M3 conversion equals that of the
-// exact quotient (binary32 carries more than 4 + 2 significant bits).
-__device__ __forceinline__ float fp8_ro_quotient(float x, float s)
+// Round-to-odd binary32 value of the exact quotient |x| / s, with the sign
+// of x and clamped to 448; its round-to-nearest-even E4M3 conversion equals
+// that of the exact quotient (binary32 carries more than 4 + 2 significant
+// bits).  rs is the hardware reciprocal of s (within 1 ulp):
+//   y0 = |x| * rs is within 3 ulp of the quotient q,
+//   y1 = y0 + fma(-y0, s, |x|) * rs is within 1/2 ulp (plus 2^-20 ulp) of q,
+//   and the sign of r = fma(-y1, s, |x|) (zero only when y1 = q) says on
+//   which side of y1 the quotient lies.
+// The residuals must not underflow: callers pass s >= 2^-64 (smaller block
+// scales are handled by multiplying x and s by 2^64).
+__device__ __forceinline__ float fp8_ro_quotient(float x, float s, float rs)
 {
     const float ax = fabsf(x);
-    const float y = ax / s;
-    const float r = __builtin_fmaf(-y, s, ax);
-    uint32_t t = __float_as_uint(y);
+    const float y0 = ax * rs;
+    const float y1 = __builtin_fmaf(__builtin_fmaf(-y0, s, ax), rs, y0);
+    const float r = __builtin_fmaf(-y1, s, ax);
+    uint32_t t = __float_as_uint(y1);
     t = (t - (r < 0.0f ? 1u : 0u)) | (r != 0.0f ? 1u : 0u);
     const float yo = fminf(__uint_as_float(t), 448.0f);
     return __uint_as_float(__float_as_uint(yo) | (__float_as_uint(x) & 0x80000000u));
+}
+
+__device__ __forceinline__ void fp8_codes(const float (&v)[32], float k, float sk, uint32_t (&d)[8])
+{
+    const float rs = __builtin_amdgcn_rcpf(sk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float* x = v + 4 * i;
+        uint32_t w = fp8_pair(fp8_ro_quotient(x[0] * k, sk, rs), fp8_ro_quotient(x[1] * k, sk, rs), 0u, false);
+        d[i] = fp8_pair(fp8_ro_quotient(x[2] * k, sk, rs), fp8_ro_quotient(x[3] * k, sk, rs), w, true);
+    }
 }
 
 __device__ __forceinline__ Fp8Words fp8_encode_block(const float (&v)[32])
@@ -369,14 +387,13 @@ __device__ __forceinline__ Fp8Words fp8_encode_block(const float (&v)[32])
     const float s = (a == __builtin_inff()) ? a : div_by<448>(a);   // inf / 448 = inf
     const bool zero = !(s >= 0x1p-126f);
     o.s = zero ? 0.0f : s;
-    const float sd = zero ? 1.0f : s;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-        const float* x = v + 4 * d;
-        uint32_t w = fp8_pair(fp8_ro_quotient(x[0], sd), fp8_ro_quotient(x[1], sd), 0u, false);
-        w = fp8_pair(fp8_ro_quotient(x[2], sd), fp8_ro_quotient(x[3], sd), w, true);
-        o.d[d] = zero ? 0u : w;
+    if (!(s < 0x1p-64f)) {
+        fp8_codes(v, 1.0f, s, o.d);
+    } else {                                  // tiny scale: x * 2^64 and s * 2^64 are exact
+        fp8_codes(v, 0x1p64f, s * 0x1p64f, o.d);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.d[i] = zero ? 0u : o.d[i];
     return o;
 }
 

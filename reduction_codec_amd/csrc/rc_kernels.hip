@@ -1,9 +1,11 @@
 // rc_kernels.hip -- gfx950 kernels of the codec and their launchers.
 //
 // One wave64 per 2048-element tile, lane l = block l; 256-thread workgroups
-// (four tiles).  Every per-lane load and store is a contiguous span across
-// the wave: code words at lane * (bytes per block), scales at lane * (scale
-// bytes), input elements at lane * 32.
+// (four waves).  Packed tiles are read and written with per-lane buffer
+// accesses that are contiguous across the wave (code words at lane * bytes
+// per block, scales at lane * scale bytes); the 64- or 128-byte element rows
+// of quantize input and unpack output are regrouped through LDS so that HBM
+// sees wave-coalesced 16-byte chunks.
 #include "rc_device.hpp"
 #include "rc_internal.hpp"
 
@@ -16,6 +18,15 @@
 #ifndef RC_REDUCE_BATCH
 #define RC_REDUCE_BATCH 2                          // streams loaded together, INT / MX
 #endif
+#ifndef RC_QUANT_WAVES
+#define RC_QUANT_WAVES 8                           // quantize occupancy target, waves per SIMD
+#endif
+#ifndef RC_QUANT_LDS
+#define RC_QUANT_LDS 1                             // quantize input regrouped through LDS
+#endif
+#ifndef RC_UNPACK_LDS
+#define RC_UNPACK_LDS 1                            // unpack output regrouped through LDS
+#endif
 
 namespace rc {
 
@@ -25,35 +36,7 @@ template <> struct TileBytes<kInt3> { static constexpr int v = 896; };
 template <> struct TileBytes<kFp8> { static constexpr int v = 2304; };
 template <> struct TileBytes<kMx4> { static constexpr int v = 1088; };
 
-__device__ __forceinline__ size_t tile_index() { return (size_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// ------------------------------------------------------------- stores ----
-
-template <int FMT>
-__device__ __forceinline__ void encode_store(const float (&v)[32], uint8_t* __restrict__ t, int lane)
-{
-    if constexpr (FMT == kInt3) {
-        const Int3Words w = int3_encode_block(v);
-        *reinterpret_cast<uint2*>(t + 8 * lane) = make_uint2(w.w0, w.w1);
-        *reinterpret_cast<uint32_t*>(t + 512 + 4 * lane) = w.h;
-        *reinterpret_cast<uint16_t*>(t + 768 + 2 * lane) = (uint16_t)w.sbits;
-    } else if constexpr (FMT == kInt4) {
-        const Int4Words w = int4_encode_block(v);
-        *reinterpret_cast<uint4*>(t + 16 * lane) = make_uint4(w.d[0], w.d[1], w.d[2], w.d[3]);
-        *reinterpret_cast<uint16_t*>(t + 1024 + 2 * lane) = (uint16_t)w.sbits;
-    } else if constexpr (FMT == kFp8) {
-        const Fp8Words w = fp8_encode_block(v);
-        uint4* p = reinterpret_cast<uint4*>(t + 32 * lane);
-        p[0] = make_uint4(w.d[0], w.d[1], w.d[2], w.d[3]);
-        p[1] = make_uint4(w.d[4], w.d[5], w.d[6], w.d[7]);
-        *reinterpret_cast<float*>(t + 2048 + 4 * lane) = w.s;
-    } else {
-        const MxWords w = mx_encode_block(v);
-        *reinterpret_cast<uint4*>(t + 16 * lane) = make_uint4(w.d[0], w.d[1], w.d[2], w.d[3]);
-        t[1024 + lane] = (uint8_t)w.e8;
-    }
-}
 
 // Per-lane code words of one block of one stream.
 template <int FMT> struct LaneCodes;
@@ -61,29 +44,6 @@ template <> struct LaneCodes<kInt3> { uint2 q2; uint32_t h; uint32_t s; };
 template <> struct LaneCodes<kInt4> { uint4 d; uint32_t s; };
 template <> struct LaneCodes<kFp8> { uint4 d0, d1; float s; };
 template <> struct LaneCodes<kMx4> { uint4 d; uint32_t e8; };
-
-template <int FMT>
-__device__ __forceinline__ LaneCodes<FMT> load_codes(const uint8_t* __restrict__ t, int lane)
-{
-    LaneCodes<FMT> c;
-    if constexpr (FMT == kInt3) {
-        c.q2 = *reinterpret_cast<const uint2*>(t + 8 * lane);
-        c.h = *reinterpret_cast<const uint32_t*>(t + 512 + 4 * lane);
-        c.s = *reinterpret_cast<const uint16_t*>(t + 768 + 2 * lane);
-    } else if constexpr (FMT == kInt4) {
-        c.d = *reinterpret_cast<const uint4*>(t + 16 * lane);
-        c.s = *reinterpret_cast<const uint16_t*>(t + 1024 + 2 * lane);
-    } else if constexpr (FMT == kFp8) {
-        const uint4* p = reinterpret_cast<const uint4*>(t + 32 * lane);
-        c.d0 = p[0];
-        c.d1 = p[1];
-        c.s = *reinterpret_cast<const float*>(t + 2048 + 4 * lane);
-    } else {
-        c.d = *reinterpret_cast<const uint4*>(t + 16 * lane);
-        c.e8 = t[1024 + lane];
-    }
-    return c;
-}
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -172,23 +132,6 @@ __device__ __forceinline__ void accumulate(const LaneCodes<FMT>& c, float (&acc)
     }
 }
 
-// ------------------------------------------------------------ kernels ----
-//
-// Global memory is touched only by wave-coalesced 16-byte accesses: a tile
-// (or a stream's tile) is read as consecutive 16-byte chunks, chunk c by lane
-// c % 64, with non-temporal hints, and staged through LDS so that each lane
-// then reads its own block.  Unpack output goes the other way.
-
-// Chunk handled by `lane` in load round r of a span of nch 16-byte chunks.
-// Lanes past the end repeat the last chunk (an in-bounds duplicate: same
-// cache line, same LDS bytes), which keeps every load and LDS write
-// unconditional.
-__device__ __forceinline__ int chunk_of(int r, int lane, int nch)
-{
-    const int c = 64 * r + lane;
-    return c < nch ? c : nch - 1;
-}
-
 __device__ __forceinline__ void wave_lds_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -211,42 +154,11 @@ __device__ __forceinline__ void store_sums_tail(float* __restrict__ sum_out, siz
         if (base + e < n) sum_out[base + e] = acc[e];
 }
 
-template <int DT>
-__device__ __forceinline__ void widen_row(const uint8_t* row, float (&v)[32])
-{
-    if constexpr (DT == kF32) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const u32x4 u = *reinterpret_cast<const u32x4*>(row + 16 * i);
-            v[4 * i] = __uint_as_float(u.x); v[4 * i + 1] = __uint_as_float(u.y);
-            v[4 * i + 2] = __uint_as_float(u.z); v[4 * i + 3] = __uint_as_float(u.w);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) widen8<DT>(*reinterpret_cast<const u32x4*>(row + 16 * i), v + 8 * i);
-    }
-}
+// ------------------------------------------------------------ kernels ----
 
-// R rounds of wave-coalesced 16-byte non-temporal loads of a span of nch
-// chunks starting at p (chunk_of() keeps every lane in bounds).
-template <int R>
-__device__ __forceinline__ void load_chunks(const uint8_t* __restrict__ p, int lane, int nch, u32x4 (&c)[R])
-{
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        c[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + chunk_of(r, lane, nch));
-}
-
-template <int R>
-__device__ __forceinline__ void stage_chunks(uint8_t* lds, int lane, int nch, const u32x4 (&c)[R])
-{
-#pragma unroll
-    for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(lds + 16 * chunk_of(r, lane, nch)) = c[r];
-}
-
-// Persistent tile loop: each wave walks tiles first, first + stride, ... and
-// loads the next tile's data while it processes the current one.  `first`
-// and `stride` are wave-uniform (scalar registers).
+// Tile walk: each wave processes tiles first, first + stride, ...; `first`
+// and `stride` are wave-uniform (scalar registers), so tile addresses and
+// buffer descriptors are built with scalar arithmetic.
 struct TileWalk {
     size_t first, stride;
     int lane, w;
@@ -262,49 +174,74 @@ __device__ __forceinline__ TileWalk tile_walk()
     return t;
 }
 
+// The 32 input elements of lane's block from the CPB 16-byte chunks of its
+// row, widened exactly to binary32.
+template <int DT, int CPB>
+__device__ __forceinline__ void widen_chunks(const u32x4 (&c)[CPB], float (&v)[32])
+{
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[4 * i] = __uint_as_float(c[i].x); v[4 * i + 1] = __uint_as_float(c[i].y);
+            v[4 * i + 2] = __uint_as_float(c[i].z); v[4 * i + 3] = __uint_as_float(c[i].w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) widen8<DT>(c[i], v + 8 * i);
+    }
+}
+
+// One wave quantizes one whole tile per iteration.  With RC_QUANT_LDS the
+// tile's input is read as wave-coalesced 16-byte chunks (chunk c by lane
+// c % 64) and regrouped through a padded LDS row per block; otherwise each
+// lane reads its own block's 16-byte chunks directly.  Codes and scales go
+// out through buffer stores.  Latency is covered by the other waves of the
+// SIMD (no in-wave prefetch).  The partial last tile, if any, is done after
+// the loop by the wave whose walk would reach it.
 template <int FMT, int DT>
-__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ in, size_t n,
-                                                       uint8_t* __restrict__ out, size_t tiles)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RC_QUANT_WAVES)))
+void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict__ out, size_t tiles)
 {
     constexpr int ES = (DT == kF32) ? 4 : 2;
     constexpr int TIB = kTile * ES;            // input bytes of one tile
     constexpr int BB = kBlock * ES;            // input bytes of one block
-    constexpr int ROW = BB + 16;               // padded LDS row: conflict-free 16-byte reads
-    constexpr int CPB = BB / 16;               // chunks per block = load rounds per lane
-    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    constexpr int CPB = BB / 16;               // 16-byte chunks per block
+    constexpr int TB = TileBytes<FMT>::v;
     const TileWalk tw = tile_walk();
-    const int lane = tw.lane;
-    const uint8_t* src = static_cast<const uint8_t*>(in);
-    const size_t full = (n % kTile) ? tiles - 1 : tiles;          // tiles without a tail
-    size_t tile = tw.first;
-    if (tile < full) {
-        u32x4 cur[CPB];
-        load_chunks<CPB>(src + tile * TIB, lane, 64 * CPB, cur);
-        for (;;) {
-            const size_t next = tile + tw.stride;
-            const bool more = next < full;
-            u32x4 nxt[CPB];
-            if (more) load_chunks<CPB>(src + next * TIB, lane, 64 * CPB, nxt);
-            wave_lds_sync();                       // previous tile's rows fully read
-#pragma unroll
-            for (int i = 0; i < CPB; ++i) {
-                const int ch = 64 * i + lane;
-                *reinterpret_cast<u32x4*>(&sm[tw.w][(ch / CPB) * ROW + (ch % CPB) * 16]) = cur[i];
-            }
-            wave_lds_sync();
-            float v[32];
-            widen_row<DT>(&sm[tw.w][lane * ROW], v);
-            encode_store<FMT>(v, out + tile * TileBytes<FMT>::v, lane);
-            if (!more) break;
-#pragma unroll
-            for (int i = 0; i < CPB; ++i) cur[i] = nxt[i];
-            tile = next;
-        }
-    }
-    if (full != tiles && (tiles - 1) % tw.stride == tw.first) {   // the partial last tile
+    const uint32_t lane = (uint32_t)tw.lane;
+    const size_t full = n / kTile;
+#if RC_QUANT_LDS
+    constexpr int ROW = BB + 16;               // padded LDS row: conflict-free 16-byte reads
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    uint8_t* lds = sm[tw.w];
+#endif
+    for (size_t tile = tw.first; tile < full; tile += tw.stride) {
+        const Rsrc src = span_rsrc(in, tile * TIB, TIB);
+        u32x4 c[CPB];
         float v[32];
-        load_block<DT>(in, (tiles - 1) * kTile + (size_t)lane * kBlock, n, v);
-        encode_store<FMT>(v, out + (tiles - 1) * TileBytes<FMT>::v, lane);
+#if RC_QUANT_LDS
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (64u * i + lane) * 16u, 0, kNT);
+        wave_lds_sync();                       // the previous tile's rows are fully read
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) {
+            const uint32_t ch = 64u * i + lane;
+            *reinterpret_cast<u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16) = c[i];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) c[i] = *reinterpret_cast<const u32x4*>(lds + lane * ROW + 16 * i);
+#else
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, lane * BB + 16u * i, 0, kNT);
+#endif
+        widen_chunks<DT, CPB>(c, v);
+        encode_store_buf<FMT>(v, span_rsrc(out, tile * TB, TB), lane);
+    }
+    if (full != tiles && full % tw.stride == tw.first) {     // the partial last tile
+        float v[32];
+        load_block<DT>(in, full * kTile + (size_t)lane * kBlock, n, v);
+        encode_store_buf<FMT>(v, span_rsrc(out, full * TB, TB), lane);
     }
 }
 
@@ -426,57 +363,55 @@ __device__ __forceinline__ void store_block_guarded(void* __restrict__ out, size
     }
 }
 
+// One wave unpacks one tile per iteration: codes in through per-lane buffer
+// loads, decoded values out either through a padded LDS row per block and
+// wave-coalesced 16-byte stores (RC_UNPACK_LDS) or straight from each lane.
 template <int FMT, int ODT>
-__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ in, size_t n,
-                                                     void* __restrict__ out, size_t tiles)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
+void unpack_kernel(const uint8_t* __restrict__ in, size_t n, void* __restrict__ out, size_t tiles)
 {
     constexpr int TB = TileBytes<FMT>::v;
-    constexpr int NCH = TB / 16;
-    constexpr int RND = (NCH + 63) / 64;
     constexpr int ES = (ODT == kF32) ? 4 : 2;
     constexpr int OB = kBlock * ES;            // output bytes of one block
-    constexpr int ROW = OB + 16;
     constexpr int CPB = OB / 16;
-    __shared__ __attribute__((aligned(16))) uint8_t smi[kWavesPerGroup][TB];
-    __shared__ __attribute__((aligned(16))) uint8_t smo[kWavesPerGroup][64 * ROW];
     const TileWalk tw = tile_walk();
-    const int lane = tw.lane;
-    size_t tile = tw.first;
-    if (tile >= tiles) return;
-    u32x4 cur[RND];
-    load_chunks<RND>(in + tile * TB, lane, NCH, cur);
-    for (;;) {
-        const size_t next = tile + tw.stride;
-        const bool more = next < tiles;
-        u32x4 nxt[RND];
-        if (more) load_chunks<RND>(in + next * TB, lane, NCH, nxt);
-        wave_lds_sync();
-        stage_chunks<RND>(smi[tw.w], lane, NCH, cur);
-        wave_lds_sync();
+    const uint32_t lane = (uint32_t)tw.lane;
+    const size_t full = n / kTile;
+#if RC_UNPACK_LDS
+    constexpr int ROW = OB + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    uint8_t* lds = sm[tw.w];
+#endif
+    for (size_t tile = tw.first; tile < full; tile += tw.stride) {
         float d[32];
-        accumulate<FMT, true>(load_codes<FMT>(smi[tw.w], lane), d);
-        const size_t base = tile * kTile + (size_t)lane * kBlock;
-        if (tile == tiles - 1 && (n % kTile) != 0) {
-            store_block_guarded<ODT>(out, base, n, d);
-        } else {
-            uint32_t wd[32];
-            out_words<ODT>(d, wd);
+        accumulate<FMT, true>(load_codes_buf<FMT>(span_rsrc(in, tile * TB, TB), lane), d);
+        uint32_t wd[32];
+        out_words<ODT>(d, wd);
+        const Rsrc dst = span_rsrc(out, tile * (size_t)(kTile * ES), kTile * ES);
+#if RC_UNPACK_LDS
+        wave_lds_sync();                       // the previous tile's rows are fully read
 #pragma unroll
-            for (int i = 0; i < CPB; ++i)
-                *reinterpret_cast<u32x4*>(&smo[tw.w][lane * ROW + 16 * i]) =
-                    (u32x4){wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]};
-            wave_lds_sync();
-            u32x4* q = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(out) + tile * (size_t)(kTile * ES));
+        for (int i = 0; i < CPB; ++i)
+            *reinterpret_cast<u32x4*>(lds + lane * ROW + 16 * i) =
+                (u32x4){wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]};
+        wave_lds_sync();
 #pragma unroll
-            for (int i = 0; i < CPB; ++i) {
-                const int ch = 64 * i + lane;
-                q[ch] = *reinterpret_cast<const u32x4*>(&smo[tw.w][(ch / CPB) * ROW + (ch % CPB) * 16]);
-            }
+        for (int i = 0; i < CPB; ++i) {
+            const uint32_t ch = 64u * i + lane;
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16),
+                                                   dst, ch * 16u, 0, kNT);
         }
-        if (!more) break;
+#else
 #pragma unroll
-        for (int r = 0; r < RND; ++r) cur[r] = nxt[r];
-        tile = next;
+        for (int i = 0; i < CPB; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]},
+                                                   dst, lane * OB + 16u * i, 0, kNT);
+#endif
+    }
+    if (full != tiles && full % tw.stride == tw.first) {     // the partial last tile
+        float d[32];
+        accumulate<FMT, true>(load_codes_buf<FMT>(span_rsrc(in, full * TB, TB), lane), d);
+        store_block_guarded<ODT>(out, full * kTile + (size_t)lane * kBlock, n, d);
     }
 }
 

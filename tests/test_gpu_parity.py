@@ -119,6 +119,50 @@ def test_quantize_is_deterministic(fmt):
 
 # -------------------------------------------------------------- unpack ----
 
+# E4M3 magnitudes of codes 0..126 from the format's definition (bias 7,
+# subnormals m * 2^-9), in increasing order
+E4M3_VALUES = [float(np.ldexp(8 + (c & 7), (c >> 3) - 10)) if c >> 3 else float(np.ldexp(c & 7, -9))
+               for c in range(127)]
+
+
+def fp8_near_midpoints(blocks: int, seed: int, emin: int, emax: int) -> np.ndarray:
+    """fp32 blocks whose FP8 scale RN32(a / 448) lies near [2^emin, 2^emax)
+    and whose other elements sit within 2 ulp of the scale times an E4M3
+    rounding midpoint, where the exact quotient decides the code."""
+    r = np.random.default_rng(seed)
+    v = np.zeros(32 * blocks, dtype=np.float32)
+    for b in range(blocks):
+        a = np.float32(np.ldexp(1.0 + r.random(), int(r.integers(emin, emax)))) * np.float32(448.0)
+        s = np.float32(a) / np.float32(448.0)
+        v[32 * b] = a if r.random() < 0.5 else -a
+        for i in range(1, 32):
+            c = int(r.integers(0, 126))
+            x = np.float32((E4M3_VALUES[c] + E4M3_VALUES[c + 1]) / 2 * float(s))
+            x = np.frombuffer((np.array([x]).view(np.int32) + np.int32(r.integers(-2, 3))).tobytes(),
+                              dtype=np.float32)[0]
+            v[32 * b + i] = -x if r.random() < 0.5 else x
+    return v
+
+
+@pytest.mark.parametrize("emin,emax", [(-126, -100), (-100, -64), (-64, -8), (-8, 40)])
+def test_fp8_quotients_next_to_midpoints(emin, emax):
+    """FP8 codes round the exact quotient x / s: inputs next to rounding
+    midpoints, over block scales from the smallest normal up (tiny scales are
+    where a residual of the quotient could underflow)."""
+    say(f"case fp8 midpoints scales 2^{emin}..2^{emax}")
+    x = fp8_near_midpoints(200, seed=emin + 1000, emin=emin, emax=emax)
+    ref = oracle_pack("fp8", x, "fp32")
+    got = host_u8(rca.quantize_pack(to_dev(x, "fp32"), rca.FP8))
+    assert_same(got, ref, "fp8 codes")
+    # the same blocks as two reduce streams (requantization of their sums)
+    y = fp8_near_midpoints(200, seed=emin + 2000, emin=emin, emax=emax)
+    streams = [ref, oracle_pack("fp8", y, "fp32")]
+    n = x.size
+    want, _ = oracle.dequant_reduce_requant(oracle.CODECS["fp8"], streams, n)
+    out, _ = rca.dequant_reduce_requant([torch.from_numpy(t).to(DEV) for t in streams], rca.FP8, n)
+    assert_same(host_u8(out), want, "fp8 reduce")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("odt", DTYPES)
 def test_unpack_dequant_bit_exact(fmt, odt):
