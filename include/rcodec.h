@@ -30,8 +30,10 @@
  *
  * Numerics (bit-exact with the CPU oracle under oracle/):
  *   INT4/INT3: s = fp16(min(fp32(absmax / qmax), 65504)) with qmax = 7 / 3;
- *     magnitude = min(round-half-even(|v| / s), qmax) of the exact quotient,
- *     sign = sign bit of v; a block whose s is 0 is stored as all-zero bytes.
+ *     magnitude = min(round-half-even(fp32(|v| * fp32(1 / s))), qmax) (one
+ *     binary32 multiply by the correctly rounded reciprocal, then the nearest
+ *     integer), sign = sign bit of v; a block whose s is 0 is stored as
+ *     all-zero bytes.
  *   FP8: s = fp32(absmax / 448), flushed to 0 below FLT_MIN (block stored as
  *     zeros); code = E4M3 round-to-nearest-even of the exact quotient v / s,
  *     saturating at 448, sign kept.  Decode = fp32(code * s).
