@@ -10,13 +10,22 @@
 #include "rc_internal.hpp"
 
 #ifndef RC_GROUPS_PER_CU
-#define RC_GROUPS_PER_CU 64                        // grid cap, workgroups per CU
+#define RC_GROUPS_PER_CU 256                       // grid cap, workgroups per CU
 #endif
 #ifndef RC_REDUCE_WAVES
 #define RC_REDUCE_WAVES 8                          // reduce occupancy target (waves per SIMD), INT / MX
 #endif
 #ifndef RC_REDUCE_BATCH
 #define RC_REDUCE_BATCH 2                          // streams loaded together, INT / MX
+#endif
+#ifndef RC_FP8_REDUCE_BATCH
+#define RC_FP8_REDUCE_BATCH 4                      // streams loaded together, FP8
+#endif
+#ifndef RC_FP8_REDUCE_WAVES
+#define RC_FP8_REDUCE_WAVES 4                      // reduce occupancy target, FP8
+#endif
+#ifndef RC_REDUCE_SCHED_BARRIER
+#define RC_REDUCE_SCHED_BARRIER 1                  // keep each batch's loads below the previous batch
 #endif
 #ifndef RC_QUANT_WAVES
 #define RC_QUANT_WAVES 8                           // quantize occupancy target, waves per SIMD
@@ -246,9 +255,9 @@ void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict_
 }
 
 // Streams whose codes are loaded together before they are accumulated.
-// FP8's encoder holds more registers: it runs at 6 waves per SIMD (80 VGPRs).
-template <int FMT> struct ReduceBatch { static constexpr int v = (FMT == kFp8) ? 2 : RC_REDUCE_BATCH; };
-template <int FMT> struct ReduceWaves { static constexpr int v = (FMT == kFp8) ? 6 : RC_REDUCE_WAVES; };
+// FP8's encoder holds more registers: it runs at fewer waves per SIMD.
+template <int FMT> struct ReduceBatch { static constexpr int v = (FMT == kFp8) ? RC_FP8_REDUCE_BATCH : RC_REDUCE_BATCH; };
+template <int FMT> struct ReduceWaves { static constexpr int v = (FMT == kFp8) ? RC_FP8_REDUCE_WAVES : RC_REDUCE_WAVES; };
 
 // acc = the K streams' decoded values of lane's block of `tile`, added in
 // stream order in binary32.
@@ -271,7 +280,7 @@ __device__ __forceinline__ void reduce_tile(const StreamPtrs& ins, size_t tile, 
         }
         // keep the next batch's loads below this batch's arithmetic (bounds
         // the registers held by codes in flight)
-        if (k0 + B < K) __builtin_amdgcn_sched_barrier(0);
+        if (RC_REDUCE_SCHED_BARRIER && k0 + B < K) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -426,8 +435,9 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ in,
 
 
 // Grid of four-wave workgroups: one tile per wave up to RC_GROUPS_PER_CU
-// workgroups per compute unit (about 1 GiB of bf16 input on 256 CUs);
-// beyond that each wave walks several tiles.
+// workgroups per compute unit (1 GiB of bf16 input on 256 CUs; measured
+// faster there than a 4x smaller grid walking 4 tiles per wave); beyond that
+// each wave walks several tiles.
 static inline dim3 tile_grid(size_t tiles)
 {
     int dev = 0, cus = 256;
