@@ -24,7 +24,7 @@ TILE = 2048
 BLOCK = 32
 MAX_STREAMS = 16
 
-FMT_INT4, FMT_INT3, FMT_FP8_E4M3, FMT_MXFP4 = 1, 2, 3, 4
+FMT_INT4, FMT_INT3, FMT_FP8_E4M3, FMT_MXFP4, FMT_FP8_E5M2 = 1, 2, 3, 4, 5
 SCALE_FP16, SCALE_FP32, SCALE_E8M0 = 1, 2, 3
 DT_FP32, DT_FP16, DT_BF16 = 1, 2, 3
 OK, ERR_NULL, ERR_UNSUPPORTED, ERR_ALIGN, ERR_RANGE, ERR_HIP = 0, 1, 2, 3, 4, 5
@@ -34,6 +34,17 @@ INT3 = (FMT_INT3, SCALE_FP16, BLOCK)
 FP8 = (FMT_FP8_E4M3, SCALE_FP32, BLOCK)
 MXFP4 = (FMT_MXFP4, SCALE_E8M0, BLOCK)
 CODECS = {"int4": INT4, "int3": INT3, "fp8": FP8, "mxfp4": MXFP4}
+
+# Every supported codec, named "<element>_<scale>_b<block>": INT4/INT3 with
+# FP16 or E8M0 scales, E4M3/E5M2 with FP32, FP16 or E8M0 scales, E2M1 with
+# E8M0 scales, blocks of 16, 32 and 64.
+_ELEMS = {"int4": FMT_INT4, "int3": FMT_INT3, "e4m3": FMT_FP8_E4M3, "e5m2": FMT_FP8_E5M2,
+          "e2m1": FMT_MXFP4}
+_SCALES = {"f16": SCALE_FP16, "f32": SCALE_FP32, "e8m0": SCALE_E8M0}
+_SUPPORTED = {"int4": ("f16", "e8m0"), "int3": ("f16", "e8m0"), "e4m3": ("f32", "f16", "e8m0"),
+              "e5m2": ("f32", "f16", "e8m0"), "e2m1": ("e8m0",)}
+ALL_CODECS = {f"{el}_{sc}_b{b}": (_ELEMS[el], _SCALES[sc], b)
+              for el, scs in _SUPPORTED.items() for sc in scs for b in (16, 32, 64)}
 
 
 class Codec(ctypes.Structure):
@@ -73,6 +84,12 @@ def _load():
         "rco_int_scale_bits": (ctypes.c_uint16, [ctypes.c_float, i32]),
         "rco_fp8_scale": (ctypes.c_float, [ctypes.c_float]),
         "rco_mx_exponent": (i32, [ctypes.c_float]),
+        "rco_e5m2_decode": (ctypes.c_float, [ctypes.c_uint8]),
+        "rco_e5m2_mag_of_quotient": (i32, [ctypes.c_double, ctypes.c_double]),
+        "rco_elem_emax": (i32, [i32]),
+        "rco_e8m0_exponent": (i32, [ctypes.c_float, i32]),
+        "rco_fp8_scale_f32": (ctypes.c_float, [ctypes.c_float, i32]),
+        "rco_fp8_scale_f16_bits": (ctypes.c_uint16, [ctypes.c_float, i32]),
     }
     for name in ("rco_map_f32_to_f16", "rco_map_f32_to_bf16", "rco_map_f16_to_f32",
                  "rco_map_bf16_to_f32", "rco_map_e4m3_mag", "rco_map_e2m1_mag",
@@ -80,6 +97,9 @@ def _load():
         sig[name] = (None, [vp, vp, sz] if "e4m3" not in name else [vp, vp, vp, sz])
     sig["rco_map_int_mag"] = (None, [vp, vp, i32, vp, sz])
     sig["rco_map_int_scale_bits"] = (None, [vp, i32, vp, sz])
+    sig["rco_map_e5m2_mag"] = (None, [vp, vp, vp, sz])
+    sig["rco_map_e8m0_exponent"] = (None, [vp, i32, vp, sz])
+    sig["rco_map_fp8_scale_f16_bits"] = (None, [vp, i32, vp, sz])
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
         f.restype, f.argtypes = res, args
@@ -140,6 +160,8 @@ def quantize_pack(c, x: np.ndarray, dtype: int | None = None, tiles: tuple[int, 
 
 def unpack_dequant(c, packed: np.ndarray, n: int, out_dtype: int = DT_FP32) -> np.ndarray:
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    if packed.size < packed_bytes(c, n):
+        raise ValueError("packed must hold packed_bytes(codec, n) bytes")
     out = np.empty(n, dtype=np.float32 if out_dtype == DT_FP32 else np.uint16)
     _check(_load().rco_unpack_dequant(_codec(c), _ptr(packed), n, out_dtype, _ptr(out)))
     if out_dtype == DT_FP16:
@@ -153,6 +175,8 @@ def dequant_reduce_requant(c, streams, n: int, want_sum: bool = False,
     """Reduce K packed streams; returns (packed, sums or None)."""
     streams = [np.ascontiguousarray(s, dtype=np.uint8) for s in streams]
     k = len(streams)
+    if any(s.size < packed_bytes(c, n) for s in streams):
+        raise ValueError("every stream must hold packed_bytes(codec, n) bytes")
     arr = (ctypes.c_void_p * max(k, 1))(*[s.ctypes.data for s in streams])
     if out is None:
         out = np.zeros(packed_bytes(c, n), dtype=np.uint8)
@@ -267,3 +291,35 @@ def e2m1_decode(nib: int) -> float:
 
 def e8m0_decode(b: int) -> float:
     return _load().rco_e8m0_decode(b)
+
+
+def e5m2_decode(code: int) -> float:
+    return _load().rco_e5m2_decode(code)
+
+
+def e5m2_mag_of_quotient(num, den):
+    num = np.asarray(num, dtype=np.float64)
+    den = np.broadcast_to(np.asarray(den, dtype=np.float64), num.shape)
+    return _map("rco_map_e5m2_mag", np.int32, num, den)
+
+
+def elem_emax(fmt: int) -> int:
+    return _load().rco_elem_emax(fmt)
+
+
+def e8m0_exponent(amax, emax: int):
+    amax = np.ascontiguousarray(amax, dtype=np.float32)
+    out = np.empty(amax.size, dtype=np.int32)
+    _load().rco_map_e8m0_exponent(_ptr(amax), emax, _ptr(out), amax.size)
+    return out
+
+
+def fp8_scale_f32(amax: float, fmt: int) -> float:
+    return _load().rco_fp8_scale_f32(amax, fmt)
+
+
+def fp8_scale_f16_bits(amax, fmt: int):
+    amax = np.ascontiguousarray(amax, dtype=np.float32)
+    out = np.empty(amax.size, dtype=np.uint16)
+    _load().rco_map_fp8_scale_f16_bits(_ptr(amax), fmt, _ptr(out), amax.size)
+    return out

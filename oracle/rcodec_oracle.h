@@ -19,10 +19,16 @@
  *        Low-Precision Collectives];
  *   - E4M3 with no infinities and a single NaN mantissa pattern
  *       [FP8 Formats for Deep Learning -- abstract];
- *   - MX blocks: a shared power-of-two scale over narrow elements, and the
- *     MXFP4 direct cast
+ *   - MX blocks: a shared power-of-two scale over narrow floating-point
+ *     and integer elements, and the MXFP4 direct cast
  *       [Microscaling Data Formats for Deep Learning -- abstract;
- *        ML-SpecQD: Multi-Level Speculative Decoding with Quantized Drafts].
+ *        ML-SpecQD: Multi-Level Speculative Decoding with Quantized Drafts];
+ *   - E5M2 with IEEE infinities and NaNs, the second FP8 encoding
+ *       [FP8 Formats for Deep Learning -- abstract].
+ * Codecs are (element format, scale type, block size): INT4 and INT3 with
+ * FP16 or E8M0 scales; E4M3 and E5M2 with FP32, FP16 or E8M0 scales; E2M1
+ * (MXFP4) with E8M0 scales; blocks of 16, 32 or 64 elements.  The tile is
+ * always 2048 elements: the code region, then 2048/block scales.
  * Every step the pages leave open is fixed once here and listed as a
  * "reading" in the design notes of the repository.
  *
@@ -44,7 +50,8 @@ extern "C" {
 #define RCO_BLOCK_ELEMS 32
 #define RCO_MAX_STREAMS 16
 
-enum { RCO_FMT_INT4 = 1, RCO_FMT_INT3 = 2, RCO_FMT_FP8_E4M3 = 3, RCO_FMT_MXFP4 = 4 };
+enum { RCO_FMT_INT4 = 1, RCO_FMT_INT3 = 2, RCO_FMT_FP8_E4M3 = 3, RCO_FMT_MXFP4 = 4,
+       RCO_FMT_FP8_E5M2 = 5 };
 enum { RCO_SCALE_FP16 = 1, RCO_SCALE_FP32 = 2, RCO_SCALE_E8M0 = 3 };
 enum { RCO_DT_FP32 = 1, RCO_DT_FP16 = 2, RCO_DT_BF16 = 3 };
 enum { RCO_OK = 0, RCO_ERR_NULL = 1, RCO_ERR_UNSUPPORTED = 2, RCO_ERR_ALIGN = 3,
@@ -78,18 +85,25 @@ uint16_t rco_f32_to_f16(float x);                 /* RNE, IEEE overflow  */
 float    rco_e4m3_decode(uint8_t code);           /* OCP E4M3 ("FN")     */
 float    rco_e2m1_decode(uint8_t nibble);
 float    rco_e8m0_decode(uint8_t byte);           /* 2^(byte-127), 0xFF NaN */
+float    rco_e5m2_decode(uint8_t code);           /* IEEE-style E5M2     */
 /* magnitude code of |num|/den rounded to nearest, ties to even code,
  * saturating; num, den exact doubles, den > 0 */
 int      rco_e4m3_mag_of_quotient(double num, double den);   /* 0..126 */
 int      rco_e2m1_mag_of(double y_abs);                      /* 0..7   */
+int      rco_e5m2_mag_of_quotient(double num, double den);   /* 0..123 */
 /* INT magnitude by the reciprocal rule: min(RNE(RN32(v_abs * r)), qmax),
  * r = rco_int_recip(s) = RN32(1/s) */
 float    rco_int_recip(float s);
 int      rco_int_mag_recip(float v_abs, float r, int qmax);
 /* per-block scale rules; amax >= 0 */
 uint16_t rco_int_scale_bits(float amax, int qmax);   /* fp16 bits       */
-float    rco_fp8_scale(float amax);                  /* 0 when flushed  */
-int      rco_mx_exponent(float amax);                /* -127..127       */
+float    rco_fp8_scale(float amax);                  /* E4M3, 0 when flushed */
+int      rco_mx_exponent(float amax);                /* E2M1, -127..127 */
+/* the same rules for any element format (RCO_FMT_*) */
+int      rco_elem_emax(int format);                  /* largest element exponent */
+int      rco_e8m0_exponent(float amax, int emax);    /* -127..127       */
+float    rco_fp8_scale_f32(float amax, int format);  /* RN32(a/fmax), 0 below FLT_MIN */
+uint16_t rco_fp8_scale_f16_bits(float amax, int format); /* fp16(min(RN32(a/fmax), 65504)) */
 
 /* element-wise loops over the scalar rules above (for the pins) */
 void rco_map_f32_to_f16(const float *x, uint16_t *y, size_t n);
@@ -102,6 +116,9 @@ void rco_map_int_mag(const float *v_abs, const float *s, int qmax, int32_t *y, s
 void rco_map_int_scale_bits(const float *amax, int qmax, uint16_t *y, size_t n);
 void rco_map_fp8_scale(const float *amax, float *y, size_t n);
 void rco_map_mx_exponent(const float *amax, int32_t *y, size_t n);
+void rco_map_e5m2_mag(const double *num, const double *den, int32_t *y, size_t n);
+void rco_map_e8m0_exponent(const float *amax, int emax, int32_t *y, size_t n);
+void rco_map_fp8_scale_f16_bits(const float *amax, int format, uint16_t *y, size_t n);
 
 #ifdef __cplusplus
 }

@@ -208,3 +208,190 @@ def reduce(fmt: str, streams, n: int):
         sums[t * TILE:t * TILE + lim] = acc[:lim]
         out += encode_tile(fmt, acc)
     return out, sums
+
+
+# ---- every codec: (element format, scale type, block size) ------------------
+#
+# Element formats 1 INT4, 2 INT3, 3 E4M3, 4 E2M1, 5 E5M2; scale types 1 fp16,
+# 2 fp32, 3 E8M0.  The tile is 2048 elements: the code region (layout as
+# above, INT3 planes by 32-element groups) then 2048/block scales.
+
+def _e5m2_table():
+    import torch
+    vals = torch.arange(124, dtype=torch.uint8).view(torch.float8_e5m2).float().numpy()
+    return [Fraction(float(v)) for v in vals]
+
+
+E5M2 = _e5m2_table()
+CODE_BYTES = {1: 1024, 2: 768, 3: 2048, 4: 1024, 5: 2048}
+SCALE_SIZE = {1: 2, 2: 4, 3: 1}
+FMAX = {3: Fraction(448), 5: Fraction(57344)}
+EMAX = {1: 2, 2: 1, 3: 8, 4: 2, 5: 15}       # largest element exponent (INT: floor log2 qmax)
+
+
+def codec_tile_bytes(c) -> int:
+    fmt, sc, bl = c
+    return CODE_BYTES[fmt] + (TILE // bl) * SCALE_SIZE[sc]
+
+
+def _floor_log2(a: Fraction) -> int:
+    e = 0
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    while Fraction(2) ** e > a:
+        e -= 1
+    return e
+
+
+def _e8m0_exp(a: float, emax: int) -> int:
+    if a == 0:
+        return -127
+    return max(-127, min(127, _floor_log2(Fraction(float(a))) - emax))
+
+
+def _nibbles_to_bytes(nib) -> bytes:
+    """nib[i] at nibble i of a little-endian bitstream."""
+    out = bytearray(len(nib) // 2)
+    for i, v in enumerate(nib):
+        out[i // 2] |= (v & 15) << (4 * (i % 2))
+    return bytes(out)
+
+
+def encode_codec(c, x_f32: np.ndarray) -> bytes:
+    """Packed bytes of x under codec c = (format, scale, block): tiles of 2048
+    with a zero-padded tail; per block the scale rule, then per element the
+    nearest code (ties to the even code, saturating)."""
+    fmt, sc, bl = c
+    x = np.asarray(x_f32, dtype=np.float32)
+    out = b""
+    for t in range((x.size + TILE - 1) // TILE):
+        v = np.zeros(TILE, dtype=np.float32)
+        chunk = x[t * TILE:(t + 1) * TILE]
+        v[:chunk.size] = chunk
+        codes = [0] * TILE           # sign-magnitude code per element (format width)
+        scales = bytearray()
+        for b in range(TILE // bl):
+            vb = v[b * bl:(b + 1) * bl]
+            a = np.float32(np.max(np.abs(vb)))
+            zero = False
+            if sc == 3:
+                ex = _e8m0_exp(float(a), EMAX[fmt])
+                scales.append(ex + 127)
+                den = Fraction(2) ** ex
+            elif fmt in (1, 2):                   # INT with fp16 scale
+                h = int_scale(a, 7 if fmt == 1 else 3)
+                zero = float(h) == 0.0
+                scales += (0 if zero else int(h.view(np.uint16))).to_bytes(2, "little")
+                den = None if zero else float(h)
+            elif sc == 1:                         # FP8 with fp16 scale
+                s32 = np.float32(a) / np.float32(float(FMAX[fmt]))
+                h = np.float16(min(s32, np.float32(65504.0)))
+                zero = float(h) == 0.0
+                scales += (0 if zero else int(h.view(np.uint16))).to_bytes(2, "little")
+                den = None if zero else Fraction(float(h))
+            else:                                 # FP8 with fp32 scale
+                s = np.float32(a) / np.float32(float(FMAX[fmt]))
+                zero = s < np.finfo(np.float32).tiny
+                scales += np.float32(0.0 if zero else s).tobytes()
+                den = None if zero else Fraction(float(s))
+            for e in range(bl):
+                i = b * bl + e
+                if zero:
+                    codes[i] = 0
+                    continue
+                sign = _sign(vb[e])
+                if fmt in (1, 2):
+                    qmax = 7 if fmt == 1 else 3
+                    if sc == 1:
+                        mag = int_mag(vb[e], den, qmax)
+                    else:
+                        mag = nearest_code(Fraction(abs(float(vb[e]))) / den, [Fraction(k) for k in range(qmax + 1)])
+                    codes[i] = (sign << 3) | mag
+                elif fmt == 4:
+                    codes[i] = (sign << 3) | nearest_code(Fraction(abs(float(vb[e]))) / den, E2M1)
+                else:
+                    table = E4M3 if fmt == 3 else E5M2
+                    codes[i] = (sign << 7) | nearest_code(Fraction(abs(float(vb[e]))) / den, table)
+        if fmt in (1, 4):
+            body = _nibbles_to_bytes(codes)
+        elif fmt == 2:
+            q2w, q1w = [], []
+            for g in range(64):
+                nib = codes[32 * g:32 * g + 32]
+                N = [sum(nib[4 * j + k] << (4 * j) for j in range(8)) for k in range(4)]
+                m = 0x33333333
+                q2w += [(N[0] & m) | ((N[1] & m) << 2), (N[2] & m) | ((N[3] & m) << 2)]
+                q1w.append(((N[0] >> 3) & 0x11111111) | ((N[1] >> 2) & 0x22222222) |
+                           ((N[2] >> 1) & 0x44444444) | (N[3] & 0x88888888))
+            body = _words_to_bytes(q2w) + _words_to_bytes(q1w)
+        else:
+            body = bytes(codes)
+        out += body + bytes(scales)
+    return out
+
+
+def decode_codec(c, tile: bytes) -> np.ndarray:
+    """Exact decode of one tile to float32 (FP8 with an fp32 scale: one IEEE
+    binary32 product)."""
+    fmt, sc, bl = c
+    cb = CODE_BYTES[fmt]
+    out = np.zeros(TILE, dtype=np.float32)
+    for i in range(TILE):
+        b = i // bl
+        if fmt in (1, 4):
+            nb = (tile[i // 2] >> (4 * (i % 2))) & 15
+            mag = nb & 7
+            val = Fraction(mag) if fmt == 1 else E2M1[mag]
+            neg = bool(nb & 8)
+        elif fmt == 2:
+            g, e = divmod(i, 32)
+            w0, w1 = [int.from_bytes(tile[8 * g + 4 * k:8 * g + 4 * k + 4], "little") for k in range(2)]
+            hw = int.from_bytes(tile[512 + 4 * g:516 + 4 * g], "little")
+            k, j = e % 4, e // 4
+            W = w0 if k < 2 else w1
+            nib = (((W >> (2 * (k & 1))) & 0x33333333) | ((hw << (3 - k)) & 0x88888888)) >> (4 * j) & 15
+            val, neg = Fraction(nib & 7), bool(nib & 8)
+        else:
+            code = tile[i]
+            table = E4M3 if fmt == 3 else E5M2
+            if (fmt == 3 and (code & 127) == 127) or (fmt == 5 and (code & 127) >= 124):
+                spec = np.float32(np.nan)
+                if fmt == 5 and (code & 127) == 124:
+                    spec = np.float32(np.inf)
+                val, neg = None, bool(code & 128)
+            else:
+                val, neg = table[code & 127], bool(code & 128)
+        so = cb + b * SCALE_SIZE[sc]
+        if val is None:
+            r = spec
+        elif sc == 2:
+            s = np.frombuffer(tile[so:so + 4], dtype=np.float32)[0]
+            r = np.float32(float(val)) * s
+        elif sc == 1:
+            s = np.frombuffer(tile[so:so + 2], dtype=np.float16)[0]
+            r = np.float32(float(val * Fraction(float(s))))
+        else:
+            if tile[so] == 255:
+                r = np.float32(np.nan)
+            else:
+                r = np.float32(float(val * Fraction(2) ** (tile[so] - 127)))
+        out[i] = -r if neg else r
+    return out
+
+
+def reduce_codec(c, streams, n: int):
+    """Decode every stream, add in stream order in binary32, requantize."""
+    tb = codec_tile_bytes(c)
+    tiles = (n + TILE - 1) // TILE
+    out = b""
+    sums = np.zeros(n, dtype=np.float32)
+    for t in range(tiles):
+        acc = None
+        for s in streams:
+            d = decode_codec(c, bytes(s[t * tb:(t + 1) * tb]))
+            acc = d.copy() if acc is None else (acc + d).astype(np.float32)
+        lim = min(TILE, n - t * TILE)
+        acc[lim:] = 0.0
+        sums[t * TILE:t * TILE + lim] = acc[:lim]
+        out += encode_codec(c, acc)
+    return out, sums

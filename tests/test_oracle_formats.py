@@ -64,7 +64,7 @@ def test_packed_bytes(c, tb):
 
 
 def test_unsupported_codecs():
-    for c in [(1, 2, 32), (2, 3, 32), (3, 1, 32), (4, 1, 32), (1, 1, 16), (1, 1, 64), (9, 1, 32)]:
+    for c in [(1, 2, 32), (2, 2, 32), (4, 1, 32), (4, 2, 32), (1, 1, 8), (3, 2, 128), (5, 2, 48), (9, 1, 32), (0, 3, 32)]:
         assert oracle.tile_bytes(c) == 0
 
 
