@@ -64,6 +64,9 @@ def parse_args():
     ap.add_argument("--table", action="store_true",
                     help="per-kernel table over every format and --table-mib sizes (no JSON line)")
     ap.add_argument("--table-mib", default="16,64,256,1024")
+    ap.add_argument("--table-codecs", default="int3,int4,fp8,mxfp4",
+                    help="comma list of codec names (default names or <elem>_<scale>_b<block>), or 'all'")
+    ap.add_argument("--table-k", default="2,4,8", help="stream counts of the reduce rows")
     return ap.parse_args()
 
 
@@ -331,10 +334,12 @@ def table(args):
     for mib in [int(v) for v in args.table_mib.split(",")]:
         n = mib * (1 << 20) // 2
         x0 = torch.from_numpy(datagen.bf16_student4(2 * n, 0).view(np.int16)).view(torch.bfloat16).to(dev)
-        for fmt in ("int3", "int4", "fp8", "mxfp4"):
-            codec = rca.CODECS[fmt]
+        names = sorted(rca.ALL_CODECS) if args.table_codecs == "all" else args.table_codecs.split(",")
+        ks = [int(v) for v in args.table_k.split(",")]
+        for fmt in names:
+            codec = rca.CODECS[fmt] if fmt in rca.CODECS else rca.ALL_CODECS[fmt]
             pb = rca.packed_bytes(codec, n)
-            kmax = 8
+            kmax = max(ks)
             sets = max(1, -(-(1 << 30) // (4 * n + (kmax + 1) * pb)))
             bufs = []
             for _ in range(sets):
@@ -346,7 +351,7 @@ def table(args):
             torch.cuda.synchronize()
             rows = [("quantize_pack bf16", lambda i: rca.quantize_pack(bufs[i % sets][0], codec, out=bufs[i % sets][2]),
                      2 * n + pb, 2 * n)]
-            for K in (2, 4, 8):
+            for K in ks:
                 rows.append((f"dequant_reduce_requant K={K}",
                              (lambda K: lambda i: rca.dequant_reduce_requant(bufs[i % sets][1][:K], codec, n,
                                                                               out=bufs[i % sets][2]))(K),

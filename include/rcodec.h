@@ -10,36 +10,42 @@
  * Low-Precision Collectives).  This library is that compute on one GPU; it
  * moves no data between GPUs.
  *
- * Data layout (all formats): the stream of n elements is cut into
- * ceil(n/2048) tiles of 2048 elements, each made of 64 blocks of 32
- * consecutive elements with one scale per block.  Positions of the last tile
- * beyond n are taken as +0.  Packed size = ceil(n/2048) * rc_tile_bytes().
+ * Data layout (all codecs): the stream of n elements is cut into
+ * ceil(n/2048) tiles of 2048 elements; each tile is its code region
+ * followed by 2048/block scales (one per block of `block` consecutive
+ * elements).  Positions of the last tile beyond n are taken as +0.  Packed
+ * size = ceil(n/2048) * rc_tile_bytes().  Code regions:
  *
- *   INT4  (1152 B/tile): 1024 B of 4-bit sign/magnitude codes (element i in
- *         nibble i, low nibble first; magnitude 0..7 in bits 0-2, sign in
- *         bit 3), then 64 little-endian fp16 scales.
- *   INT3  (896 B/tile):  q2w plane (512 B, 2-bit magnitudes 0..3), q1w plane
- *         (256 B, sign of element i at bit i), then 64 fp16 scales.  Inside
- *         block b the q2w bits of element e sit at bit 64b + 32*((e/2)%2) +
- *         4*(e/4) + 2*(e%2) of the plane (element pairs dealt alternately to
- *         the block's two 32-bit words).
- *   FP8   (2304 B/tile): 2048 E4M3 codes (OCP "FN": no infinities, NaN =
- *         S.1111.111), then 64 little-endian fp32 scales.
- *   MXFP4 (1088 B/tile): 1024 B of E2M1 codes (element i in nibble i), then
- *         64 E8M0 scale bytes (2^(byte-127)).
+ *   INT4  (1024 B): 4-bit sign/magnitude codes (element i in nibble i, low
+ *         nibble first; magnitude 0..7 in bits 0-2, sign in bit 3).
+ *   INT3  (768 B):  q2w plane (512 B, 2-bit magnitudes 0..3), then q1w plane
+ *         (256 B, sign of element i at bit i).  The q2w bits of element e of
+ *         the 32-element group g (tile element 32g + e, whatever the block
+ *         size) sit at bit 64g + 32*((e/2)%2) + 4*(e/4) + 2*(e%2) of the plane
+ *         (element pairs dealt alternately to the group's two 32-bit words).
+ *   FP8_E4M3 (2048 B): E4M3 codes (OCP "FN": no infinities, NaN = S.1111.111).
+ *   FP8_E5M2 (2048 B): E5M2 codes (bias 15, IEEE infinities and NaNs).
+ *   MXFP4 (1024 B): E2M1 codes (element i in nibble i).
+ * Scales: fp16 (2 B) or fp32 (4 B) little-endian, or E8M0 bytes
+ * (2^(byte-127), 0xFF = NaN).  The default tiles: INT4 1152 B, INT3 896 B,
+ * E4M3 + FP32 2304 B, MXFP4 1088 B.
  *
  * Numerics (bit-exact with the CPU oracle under oracle/):
- *   INT4/INT3: s = fp16(min(fp32(absmax / qmax), 65504)) with qmax = 7 / 3;
- *     magnitude = min(round-half-even(fp32(|v| * fp32(1 / s))), qmax) (one
- *     binary32 multiply by the correctly rounded reciprocal, then the nearest
- *     integer), sign = sign bit of v; a block whose s is 0 is stored as
- *     all-zero bytes.
- *   FP8: s = fp32(absmax / 448), flushed to 0 below FLT_MIN (block stored as
- *     zeros); code = E4M3 round-to-nearest-even of the exact quotient v / s,
- *     saturating at 448, sign kept.  Decode = fp32(code * s).
- *   MXFP4: e = clamp(floor(log2 absmax) - 2, -127, 127) (-127 for a zero
- *     block); code = E2M1 round-to-nearest-even of v * 2^-e, saturating at 6,
- *     sign kept.
+ *   INT4/INT3, FP16 scale: s = fp16(min(fp32(absmax / qmax), 65504)) with
+ *     qmax = 7 / 3; magnitude = min(round-half-even(fp32(|v| * fp32(1 / s))),
+ *     qmax) (one binary32 multiply by the correctly rounded reciprocal, then
+ *     the nearest integer), sign = sign bit of v; a block whose s is 0 is
+ *     stored as all-zero bytes.
+ *   FP8, FP32 scale: s = fp32(absmax / fmax) (fmax = 448 for E4M3, 57344 for
+ *     E5M2), flushed to 0 below FLT_MIN (block stored as zeros); code = the
+ *     round-to-nearest-even code of the exact quotient v / s, saturating at
+ *     fmax, sign kept.  Decode = fp32(code * s).
+ *   FP8, FP16 scale: s = fp16(min(fp32(absmax / fmax), 65504)); codes as with
+ *     an FP32 scale; s = 0 stores a zero block.
+ *   E8M0 scale (any element format): e = clamp(floor(log2 absmax) - emax,
+ *     -127, 127) with emax = 2 (E2M1), 8 (E4M3), 15 (E5M2), 2 (INT4), 1
+ *     (INT3); -127 for a zero block; code = the nearest code (ties to even,
+ *     saturating at the format's largest magnitude) of v * 2^-e; signs kept.
  *   Reduce: acc = d_0; acc = fp32(acc + d_k) for k = 1..K-1 in stream order;
  *     the sums are requantized with the same codec.
  *
@@ -65,18 +71,23 @@
 extern "C" {
 #endif
 
-#define RC_ABI_VERSION 1
+#define RC_ABI_VERSION 2
 #define RC_TILE_ELEMS 2048
 #define RC_BLOCK_ELEMS 32
 #define RC_MAX_STREAMS 16
 
-typedef enum { RC_FMT_INT4 = 1, RC_FMT_INT3 = 2, RC_FMT_FP8_E4M3 = 3, RC_FMT_MXFP4 = 4 } rc_format;
+typedef enum { RC_FMT_INT4 = 1, RC_FMT_INT3 = 2, RC_FMT_FP8_E4M3 = 3, RC_FMT_MXFP4 = 4,
+               RC_FMT_FP8_E5M2 = 5 } rc_format;
 typedef enum { RC_SCALE_FP16 = 1, RC_SCALE_FP32 = 2, RC_SCALE_E8M0 = 3 } rc_scale_type;
 typedef enum { RC_DT_FP32 = 1, RC_DT_FP16 = 2, RC_DT_BF16 = 3 } rc_dtype;
 
 /* Codec = element format + scale type + block size, passed by value.
- * Supported: {INT4, FP16, 32}, {INT3, FP16, 32}, {FP8_E4M3, FP32, 32},
- * {MXFP4, E8M0, 32}; anything else is RC_ERR_UNSUPPORTED. */
+ * Supported (block 16, 32 or 64 elements in every case):
+ *   INT4, INT3          with RC_SCALE_FP16 or RC_SCALE_E8M0
+ *   FP8_E4M3, FP8_E5M2  with RC_SCALE_FP32, RC_SCALE_FP16 or RC_SCALE_E8M0
+ *   MXFP4 (E2M1)        with RC_SCALE_E8M0
+ * anything else is RC_ERR_UNSUPPORTED.  The defaults of the pages are
+ * {INT4, FP16, 32}, {INT3, FP16, 32}, {FP8_E4M3, FP32, 32}, {MXFP4, E8M0, 32}. */
 typedef struct { int32_t format, scale, block; } rc_codec;
 
 typedef enum {

@@ -27,7 +27,7 @@ TILE = 2048
 BLOCK = 32
 MAX_STREAMS = 16
 
-FMT_INT4, FMT_INT3, FMT_FP8_E4M3, FMT_MXFP4 = 1, 2, 3, 4
+FMT_INT4, FMT_INT3, FMT_FP8_E4M3, FMT_MXFP4, FMT_FP8_E5M2 = 1, 2, 3, 4, 5
 SCALE_FP16, SCALE_FP32, SCALE_E8M0 = 1, 2, 3
 DT_FP32, DT_FP16, DT_BF16 = 1, 2, 3
 OK, ERR_NULL, ERR_UNSUPPORTED, ERR_ALIGN, ERR_RANGE, ERR_HIP = 0, 1, 2, 3, 4, 5
@@ -46,6 +46,20 @@ INT3 = Codec(FMT_INT3, SCALE_FP16, BLOCK)
 FP8 = Codec(FMT_FP8_E4M3, SCALE_FP32, BLOCK)
 MXFP4 = Codec(FMT_MXFP4, SCALE_E8M0, BLOCK)
 CODECS = {"int4": INT4, "int3": INT3, "fp8": FP8, "mxfp4": MXFP4}
+
+
+def _all_codecs():
+    """Every codec the library supports, by name "<element>_<scale>_b<block>"
+    (also accepted wherever a codec is expected)."""
+    elems = {"int4": FMT_INT4, "int3": FMT_INT3, "e4m3": FMT_FP8_E4M3, "e5m2": FMT_FP8_E5M2, "e2m1": FMT_MXFP4}
+    scales = {"f16": SCALE_FP16, "f32": SCALE_FP32, "e8m0": SCALE_E8M0}
+    allowed = {"int4": ("f16", "e8m0"), "int3": ("f16", "e8m0"), "e4m3": ("f32", "f16", "e8m0"),
+               "e5m2": ("f32", "f16", "e8m0"), "e2m1": ("e8m0",)}
+    return {f"{e}_{sc}_b{b}": Codec(elems[e], scales[sc], b)
+            for e, scs in allowed.items() for sc in scs for b in (16, 32, 64)}
+
+
+ALL_CODECS = _all_codecs()
 
 _DTYPES = {torch.float32: DT_FP32, torch.float16: DT_FP16, torch.bfloat16: DT_BF16}
 _lib = None
@@ -86,7 +100,7 @@ def _codec(c) -> Codec:
     if isinstance(c, Codec):
         return c
     if isinstance(c, str):
-        return CODECS[c]
+        return CODECS[c] if c in CODECS else ALL_CODECS[c]
     return Codec(*c)
 
 

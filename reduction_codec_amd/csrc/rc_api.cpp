@@ -3,7 +3,7 @@
 // Validation never touches HIP, so every error path can be exercised on a
 // machine without a GPU.
 #include "rcodec.h"
-#include "rc_internal.hpp"
+#include "rc_launch.hpp"
 
 namespace {
 
@@ -11,13 +11,16 @@ namespace {
 // grid dimension (tiles / 4 workgroups) far inside their types.
 constexpr size_t kMaxElems = (size_t)1 << 40;
 
+// Supported codecs: INT4/INT3 with FP16 or E8M0 scales, E4M3/E5M2 with FP32,
+// FP16 or E8M0 scales, E2M1 (MXFP4) with E8M0 scales; blocks of 16, 32, 64.
 bool codec_ok(rc_codec c)
 {
-    if (c.block != RC_BLOCK_ELEMS) return false;
+    if (c.block != 16 && c.block != 32 && c.block != 64) return false;
     switch (c.format) {
-    case RC_FMT_INT4:     return c.scale == RC_SCALE_FP16;
-    case RC_FMT_INT3:     return c.scale == RC_SCALE_FP16;
-    case RC_FMT_FP8_E4M3: return c.scale == RC_SCALE_FP32;
+    case RC_FMT_INT4:
+    case RC_FMT_INT3:     return c.scale == RC_SCALE_FP16 || c.scale == RC_SCALE_E8M0;
+    case RC_FMT_FP8_E4M3:
+    case RC_FMT_FP8_E5M2: return c.scale == RC_SCALE_FP32 || c.scale == RC_SCALE_FP16 || c.scale == RC_SCALE_E8M0;
     case RC_FMT_MXFP4:    return c.scale == RC_SCALE_E8M0;
     default:              return false;
     }
@@ -35,12 +38,15 @@ extern "C" {
 size_t rc_tile_bytes(rc_codec c)
 {
     if (!codec_ok(c)) return 0;
+    size_t code;                                  // code region of 2048 elements
     switch (c.format) {
-    case RC_FMT_INT4:     return 1152;
-    case RC_FMT_INT3:     return 896;
-    case RC_FMT_FP8_E4M3: return 2304;
-    default:              return 1088;
+    case RC_FMT_INT3: code = 768; break;          // 2-bit + 1-bit planes
+    case RC_FMT_FP8_E4M3:
+    case RC_FMT_FP8_E5M2: code = 2048; break;
+    default: code = 1024;                         // 4-bit codes
     }
+    const size_t sb = c.scale == RC_SCALE_FP16 ? 2 : (c.scale == RC_SCALE_FP32 ? 4 : 1);
+    return code + (size_t)(RC_TILE_ELEMS / c.block) * sb;
 }
 
 size_t rc_packed_bytes(rc_codec c, size_t n)
@@ -55,7 +61,7 @@ rc_status rc_quantize_pack(rc_codec c, rc_dtype in_t, const void* in, size_t n, 
     if (n > kMaxElems) return RC_ERR_RANGE;
     if (!in || !out) return RC_ERR_NULL;
     if (!aligned16(in) || !aligned16(out)) return RC_ERR_ALIGN;
-    return from_hip(rc::launch_quantize(c.format, in_t, in, n, out, static_cast<hipStream_t>(stream)));
+    return from_hip(rc::launch_quantize(c.format, c.scale, c.block, in_t, in, n, out, static_cast<hipStream_t>(stream)));
 }
 
 rc_status rc_unpack_dequant(rc_codec c, const void* in, size_t n, rc_dtype out_t, void* out, void* stream)
@@ -65,7 +71,7 @@ rc_status rc_unpack_dequant(rc_codec c, const void* in, size_t n, rc_dtype out_t
     if (n > kMaxElems) return RC_ERR_RANGE;
     if (!in || !out) return RC_ERR_NULL;
     if (!aligned16(in) || !aligned16(out)) return RC_ERR_ALIGN;
-    return from_hip(rc::launch_unpack(c.format, in, n, out_t, out, static_cast<hipStream_t>(stream)));
+    return from_hip(rc::launch_unpack(c.format, c.scale, c.block, in, n, out_t, out, static_cast<hipStream_t>(stream)));
 }
 
 rc_status rc_dequant_reduce_requant(rc_codec c, const void* const* ins, int k, size_t n, void* out,
@@ -83,7 +89,7 @@ rc_status rc_dequant_reduce_requant(rc_codec c, const void* const* ins, int k, s
         p.p[j] = static_cast<const uint8_t*>(ins[j]);
     }
     if (!aligned16(out) || (sum_out && !aligned16(sum_out))) return RC_ERR_ALIGN;
-    return from_hip(rc::launch_reduce(c.format, p, k, n, out, sum_out, static_cast<hipStream_t>(stream)));
+    return from_hip(rc::launch_reduce(c.format, c.scale, c.block, p, k, n, out, sum_out, static_cast<hipStream_t>(stream)));
 }
 
 rc_status rc_copy(const void* in, void* out, size_t bytes, void* stream)

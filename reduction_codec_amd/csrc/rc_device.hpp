@@ -79,6 +79,28 @@ __device__ __forceinline__ f2 fp8_dec(uint32_t w, bool hi)
     return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
 }
 
+// The two E4M3 codes of 16-bit word `hi` of w, times the power-of-two part
+// of `scale`, exactly.
+__device__ __forceinline__ f2 fp8_dec_scaled(uint32_t w, float scale, bool hi)
+{
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w, scale, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w, scale, false);
+}
+
+// Two binary32 -> two E5M2 codes (RNE; exact for |x| <= 57344, infinity from
+// 61440 up: callers clamp) into 16-bit word `hi` of `old`.
+__device__ __forceinline__ uint32_t bf8_pair(float a, float b, uint32_t old, bool hi)
+{
+    return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, true)
+              : (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, false);
+}
+
+// The two E5M2 codes of 16-bit word `hi` of w, exactly.
+__device__ __forceinline__ f2 bf8_dec(uint32_t w, bool hi)
+{
+    return hi ? __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+}
+
 // ---------------------------------------------------------------- loads ----
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -136,12 +158,23 @@ __device__ __forceinline__ void load_block(const void* __restrict__ in, size_t b
     }
 }
 
-__device__ __forceinline__ float absmax32(const float (&v)[32])
+// max |v[e]| over e in [B, E)
+template <int B, int E>
+__device__ __forceinline__ float absmax_range(const float (&v)[32])
 {
     float a = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 32; e += 2) a = fmaxf(fmaxf(fabsf(v[e]), fabsf(v[e + 1])), a);
+    for (int e = B; e < E; e += 2) a = fmaxf(fmaxf(fabsf(v[e]), fabsf(v[e + 1])), a);
     return a;
+}
+
+__device__ __forceinline__ float absmax32(const float (&v)[32]) { return absmax_range<0, 32>(v); }
+
+// The value held by the other lane of this lane's pair (lanes 2m, 2m+1):
+// a DPP quad permutation [1,0,3,2].
+__device__ __forceinline__ float pair_swap(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
 // ------------------------------------------------------- INT scale rule ----
@@ -155,9 +188,10 @@ struct IntScale {
 };
 
 // Correctly rounded a / b for a constant b: q = a * RN(1/b), then one
-// residual correction.  For b = 3, 7 and 448 this equals the IEEE quotient
-// for every finite a >= 0 (448: wherever the quotient is normal), which an
-// exhaustive run over all binary32 inputs confirms; an infinite a gives NaN.
+// residual correction.  For b = 3, 7, 448 and 57344 this equals the IEEE
+// quotient for every finite a >= 0 (448, 57344: wherever the quotient is
+// normal), which an exhaustive run over all binary32 inputs confirms; an
+// infinite a gives NaN.
 template <int B>
 __device__ __forceinline__ float div_by(float a)
 {
@@ -194,14 +228,136 @@ __device__ __forceinline__ IntScale int_scale(float a)
 
 __device__ __forceinline__ uint32_t signbit_u(float x) { return __float_as_uint(x) >> 31; }
 
+// floor(log2 a) of a positive binary32, subnormals included (128 for inf).
+__device__ __forceinline__ int ilog2f(float a)
+{
+    const uint32_t b = __float_as_uint(a);
+    const int ef = (int)(b >> 23);
+    return ef ? ef - 127 : (31 - (int)__builtin_clz(b)) - 149;
+}
+
+// ============================================================ codecs ====
+//
+// A codec is (element format, scale type, block size).  Each lane holds 32
+// consecutive elements of a tile; with 32-element blocks that is one block,
+// with 16-element blocks two (elements 0-15 and 16-31, "halves"), and with
+// 64-element blocks lanes 2m and 2m+1 share one block (absmax exchanged
+// across the pair, the even lane stores the scale).
+
+enum : int { kS16 = 1, kS32 = 2, kSE8 = 3 };   // scale types (rc_scale_type)
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<1> { static constexpr int code_bytes = 1024, emax = 2, qmax = 7; };       // INT4
+template <> struct Fmt<2> { static constexpr int code_bytes = 768, emax = 1, qmax = 3; };        // INT3
+template <> struct Fmt<3> { static constexpr int code_bytes = 2048, emax = 8, fmax = 448; };     // E4M3
+template <> struct Fmt<4> { static constexpr int code_bytes = 1024, emax = 2; };                // E2M1
+template <> struct Fmt<5> { static constexpr int code_bytes = 2048, emax = 15, fmax = 57344; }; // E5M2
+
+template <int SC> struct ScaleBytes { static constexpr int v = SC == kS16 ? 2 : (SC == kS32 ? 4 : 1); };
+template <int BL> struct Halves { static constexpr int v = (BL == 16) ? 2 : 1; };  // scale blocks per lane
+
+template <int FMT, int SC, int BL> struct TileGeom {
+    static constexpr int code = Fmt<FMT>::code_bytes;
+    static constexpr int bytes = code + (2048 / BL) * ScaleBytes<SC>::v;
+};
+
+// MX shared exponent: floor(log2 a) minus the element format's largest
+// exponent, clamped to the E8M0 range; -127 for a zero block.
+template <int EMAX>
+__device__ __forceinline__ int e8m0_exponent(float a)
+{
+    int e = (a == 0.0f) ? -127 : ilog2f(a) - EMAX;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Per-block encode data: the stored scale bits and the element multiplier
+// (INT/FP16: fp32(1/s); E8M0: 2^-e; FP8 with FP32/FP16 scale: s itself;
+// E2M1: 2^e, the conversion's scale operand).
+struct EncScale {
+    uint32_t bits;
+    float m;
+    bool zero;       // FP16/FP32 scale 0: the block is stored as zeros
+    bool clamp;      // codes may exceed the format's largest magnitude
+};
+
+template <int FMT, int SC>
+__device__ __forceinline__ EncScale enc_scale(float a)
+{
+    EncScale r;
+    r.zero = false;
+    r.clamp = false;
+    if constexpr (FMT == 1 || FMT == 2) {
+        if constexpr (SC == kS16) {
+            const IntScale sc = int_scale<Fmt<FMT>::qmax>(a);
+            r.bits = sc.zero ? 0u : sc.bits;
+            r.m = sc.r;
+            r.zero = sc.zero;
+            r.clamp = sc.abnormal;
+        } else {
+            const int e = e8m0_exponent<Fmt<FMT>::emax>(a);
+            r.bits = (uint32_t)(e + 127);
+            r.m = __builtin_ldexpf(1.0f, -e);
+            r.clamp = true;                              // a / 2^e lies in [2^k, 2^(k+1))
+        }
+    } else if constexpr (FMT == 3 || FMT == 5) {
+        if constexpr (SC == kS32) {
+            const float s = (a == __builtin_inff()) ? a : div_by<Fmt<FMT>::fmax>(a);   // inf / fmax = inf
+            r.zero = !(s >= 0x1p-126f);
+            r.bits = r.zero ? 0u : __float_as_uint(s);
+            r.m = s;
+        } else if constexpr (SC == kS16) {
+            const float s32 = fminf(div_by<Fmt<FMT>::fmax>(a), 65504.0f);            // NaN (inf a) -> 65504
+            const __half h = __float2half_rn(s32);
+            const float s = __half2float(h);
+            r.zero = (s == 0.0f);
+            r.bits = r.zero ? 0u : (uint32_t)__half_as_ushort(h);
+            r.m = s;
+        } else {
+            const int e = e8m0_exponent<Fmt<FMT>::emax>(a);
+            r.bits = (uint32_t)(e + 127);
+            r.m = __builtin_ldexpf(1.0f, -e);
+        }
+    } else {
+        const int e = e8m0_exponent<2>(a);
+        r.bits = (uint32_t)(e + 127);
+        r.m = __builtin_ldexpf(1.0f, e);                 // 2^e, subnormal for e < -126
+    }
+    return r;
+}
+
+// The lane's block maxima: two halves, one block, or the pair's block.
+template <int BL>
+__device__ __forceinline__ void lane_absmax(const float (&v)[32], float (&a)[Halves<BL>::v])
+{
+    if constexpr (BL == 16) {
+        a[0] = absmax_range<0, 16>(v);
+        a[1] = absmax_range<16, 32>(v);
+    } else {
+        float m = absmax32(v);
+        if constexpr (BL == 64) m = fmaxf(m, pair_swap(m));
+        a[0] = m;
+    }
+}
+
+// All-ones unless the block (or half h of a 16-element-block lane) is a
+// zero-scale block; `lo`/`hi` select which 16 of the word's bits belong to
+// the first half for word layouts that mix halves (INT3 group words).
+template <int H>
+__device__ __forceinline__ uint32_t keep_mask(const EncScale (&sc)[H], int half)
+{
+    return sc[H == 2 ? half : 0].zero ? 0u : 0xFFFFFFFFu;
+}
+
 // ----------------------------------------------------------------- INT3 ----
-// Group word g (g = 0..3) of a block holds in nibble j the code of element
-// 4j + g: (sign << 3) | magnitude.  Plane words:
+// Group word g (g = 0..3) of a lane's 32 elements holds in nibble j the code
+// of element 4j + g: (sign << 3) | magnitude.  Plane words:
 //   q2w word 0 = (N0 & 0x33333333) | ((N1 & 0x33333333) << 2)
 //   q2w word 1 = (N2 & 0x33333333) | ((N3 & 0x33333333) << 2)
 //   q1w word   = sign of element e at bit e.
+// Nibbles 0-3 of a group word are elements 0..15, nibbles 4-7 elements
+// 16..31; byte b holds nibbles 2b, 2b+1 (elements 8b+g, 8b+4+g).
 
-struct Int3Words { uint32_t w0, w1, h, sbits; };
+struct Int3Words { uint32_t w0, w1, h; };
 
 __device__ __forceinline__ Int3Words int3_planes(const uint32_t (&N)[4])
 {
@@ -219,19 +375,6 @@ __device__ __forceinline__ uint32_t int3_group(uint32_t w0, uint32_t w1, uint32_
     return ((w >> (2 * (g & 1))) & 0x33333333u) | ((h << (3 - g)) & 0x88888888u);
 }
 
-// E2M1 nibbles of the 32 elements, group g in word N[g] (nibble j = element
-// 4j + g), of x * r2 with r2 = fp32(1/s) / 2.
-__device__ __forceinline__ void int3_groups(const float (&v)[32], float r2, uint32_t (&N)[4])
-{
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) w = fp4_enc(w, v[8 * b + g] * r2, v[8 * b + 4 + g] * r2, 1.0f, b);
-        N[g] = w;
-    }
-}
-
 // min(magnitude, 3) on E2M1 nibbles: a magnitude code with bit 2 set (an E2M1
 // value of 2 or more, i.e. an INT3 magnitude of 4 or more) becomes 3.
 __device__ __forceinline__ uint32_t int3_clamp_word(uint32_t w)
@@ -240,51 +383,64 @@ __device__ __forceinline__ uint32_t int3_clamp_word(uint32_t w)
     return (w & 0x88888888u) | (w & 0x33333333u) | (big * 3u);
 }
 
-__device__ __forceinline__ Int3Words int3_encode_block(const float (&v)[32])
+// INT3 codes: E2M1 nibbles of x * m / 2 (m = fp32(1/s) or 2^-e): RNE, the
+// low code bit is the integer's parity below 2; clamped when a block may
+// exceed 3.
+template <int H>
+__device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const EncScale (&sc)[H])
 {
-    const IntScale sc = int_scale<3>(absmax32(v));
-    const float r2 = 0.5f * sc.r;                       // exact
+    float r2[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) r2[h] = 0.5f * sc[h].m;                // exact
     uint32_t N[4];
-    int3_groups(v, r2, N);
-    // Only a subnormal or saturated scale lets |x| * r exceed 3 + 1/2.
-    if (sc.abnormal) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float r = r2[H == 2 ? b / 2 : 0];
+            w = fp4_enc(w, v[8 * b + g] * r, v[8 * b + 4 + g] * r, 1.0f, b);
+        }
+        N[g] = w;
+    }
+    bool clamp = sc[0].clamp;
+    if constexpr (H == 2) clamp = clamp || sc[1].clamp;
+    if (clamp) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) N[g] = int3_clamp_word(N[g]);
     }
-    const uint32_t keep = sc.zero ? 0u : 0xFFFFFFFFu;
+    uint32_t keep = sc[0].zero ? 0u : 0xFFFFFFFFu;
+    if constexpr (H == 2) keep = (sc[0].zero ? 0u : 0x0000FFFFu) | (sc[1].zero ? 0u : 0xFFFF0000u);
 #pragma unroll
     for (int g = 0; g < 4; ++g) N[g] &= keep;
-    Int3Words o = int3_planes(N);
-    o.sbits = sc.zero ? 0u : sc.bits;
-    return o;
+    return int3_planes(N);
 }
 
-// acc[e] (+)= q_e * s for the 32 elements of one INT3 block.
-template <bool FIRST>
-__device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32_t h, uint32_t sbits,
+// acc[e] (+)= q_e * S for the 32 elements: E2M1 decode of the nibble (q/2)
+// times dm = 2S (exact products, one rounding per add).
+template <bool FIRST, int H>
+__device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32_t h, const float (&dm)[H],
                                                 float (&acc)[32])
 {
-    const float s2 = 2.0f * __half2float(__ushort_as_half((unsigned short)sbits));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const uint32_t Ng = int3_group(w0, w1, h, g);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
+            const float m = dm[H == 2 ? b / 2 : 0];
             const f2 c = fp4_dec(Ng, 1.0f, b);
-            if (FIRST) { acc[8 * b + g] = c.x * s2; acc[8 * b + 4 + g] = c.y * s2; }
+            if (FIRST) { acc[8 * b + g] = c.x * m; acc[8 * b + 4 + g] = c.y * m; }
             else {
-                acc[8 * b + g] = __builtin_fmaf(c.x, s2, acc[8 * b + g]);
-                acc[8 * b + 4 + g] = __builtin_fmaf(c.y, s2, acc[8 * b + 4 + g]);
+                acc[8 * b + g] = __builtin_fmaf(c.x, m, acc[8 * b + g]);
+                acc[8 * b + 4 + g] = __builtin_fmaf(c.y, m, acc[8 * b + 4 + g]);
             }
         }
     }
 }
 
 // ----------------------------------------------------------------- INT4 ----
-// Word d (d = 0..3) of a block holds elements 8d..8d+7, element 8d+j in
-// nibble j: (sign << 3) | magnitude.  E4M3 view: byte = (sign << 7) | m.
-
-struct Int4Words { uint32_t d[4]; uint32_t sbits; };
+// Word d (d = 0..3) holds elements 8d..8d+7, element 8d+j in nibble j:
+// (sign << 3) | magnitude.  E4M3 view: byte = (sign << 7) | m.
 
 // min(magnitude, 7) on four E4M3 bytes of INT4 codes: a byte with a nonzero
 // exponent field (value 8 * 2^-9 or more) gets mantissa bits 111; only the
@@ -295,68 +451,93 @@ __device__ __forceinline__ uint32_t int4_clamp_bytes(uint32_t x)
     return x | big | (big << 1) | (big << 2);
 }
 
-__device__ __forceinline__ Int4Words int4_encode_block(const float (&v)[32])
+// INT4 codes: E4M3 subnormal bytes of x * m * 2^-9 (RNE), clamped when a
+// block may exceed 7.
+template <int H>
+__device__ __forceinline__ void int4_encode(const float (&v)[32], const EncScale (&sc)[H], uint32_t (&D)[4])
 {
-    const IntScale sc = int_scale<7>(absmax32(v));
-    const float r9 = sc.r * 0x1p-9f;                    // exact
-    // E4M3 subnormal bytes of x * r9: word d's even elements 0,2,4,6 in the
-    // bytes of xe[d], odd elements 1,3,5,7 in xo[d]
+    float r9[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) r9[h] = sc[h].m * 0x1p-9f;               // exact
+    // word d's even elements 0,2,4,6 in the bytes of xe[d], odd 1,3,5,7 in xo[d]
     uint32_t xe[4], xo[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+        const float r = r9[H == 2 ? d / 2 : 0];
         const float* y = v + 8 * d;
-        xe[d] = fp8_pair(y[4] * r9, y[6] * r9, fp8_pair(y[0] * r9, y[2] * r9, 0u, false), true);
-        xo[d] = fp8_pair(y[5] * r9, y[7] * r9, fp8_pair(y[1] * r9, y[3] * r9, 0u, false), true);
+        xe[d] = fp8_pair(y[4] * r, y[6] * r, fp8_pair(y[0] * r, y[2] * r, 0u, false), true);
+        xo[d] = fp8_pair(y[5] * r, y[7] * r, fp8_pair(y[1] * r, y[3] * r, 0u, false), true);
     }
-    // Only a subnormal or saturated scale lets |x| * r exceed 7 + 1/2.
-    if (sc.abnormal) {
+    bool clamp = sc[0].clamp;
+    if constexpr (H == 2) clamp = clamp || sc[1].clamp;
+    if (clamp) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) { xe[d] = int4_clamp_bytes(xe[d]); xo[d] = int4_clamp_bytes(xo[d]); }
     }
-    const uint32_t keep = sc.zero ? 0u : 0xFFFFFFFFu;
-    Int4Words o;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
-        o.d[d] = ((xe[d] & 0x07070707u) | ((xe[d] >> 4) & 0x08080808u) | ((xo[d] << 4) & 0x70707070u) |
-                  (xo[d] & 0x80808080u)) & keep;
-    o.sbits = sc.zero ? 0u : sc.bits;
-    return o;
+        D[d] = ((xe[d] & 0x07070707u) | ((xe[d] >> 4) & 0x08080808u) | ((xo[d] << 4) & 0x70707070u) |
+                (xo[d] & 0x80808080u)) & keep_mask(sc, d / 2);
 }
 
-template <bool FIRST>
-__device__ __forceinline__ void int4_accumulate(const uint32_t (&D)[4], uint32_t sbits, float (&acc)[32])
+// acc[e] (+)= q_e * S: the nibbles rebuilt as E4M3 subnormal bytes, decoded
+// times the power-of-two part of `cs` (1 for an FP16 scale, giving q 2^-9,
+// with dm = 512 s; 512 for E8M0, giving q, with dm = 2^e).
+template <bool FIRST, int H>
+__device__ __forceinline__ void int4_accumulate(const uint32_t (&D)[4], float cs, const float (&dm)[H],
+                                                float (&acc)[32])
 {
-    const float s9 = 512.0f * __half2float(__ushort_as_half((unsigned short)sbits));
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+        const float m = dm[H == 2 ? d / 2 : 0];
         const uint32_t xe = (D[d] & 0x07070707u) | ((D[d] << 4) & 0x80808080u);
         const uint32_t xo = ((D[d] >> 4) & 0x07070707u) | (D[d] & 0x80808080u);
-        const f2 e01 = fp8_dec(xe, false), e23 = fp8_dec(xe, true);
-        const f2 o01 = fp8_dec(xo, false), o23 = fp8_dec(xo, true);
-        const float cs[8] = {e01.x, o01.x, e01.y, o01.y, e23.x, o23.x, e23.y, o23.y};
+        f2 e01, e23, o01, o23;
+        if (cs == 1.0f) {
+            e01 = fp8_dec(xe, false); e23 = fp8_dec(xe, true);
+            o01 = fp8_dec(xo, false); o23 = fp8_dec(xo, true);
+        } else {
+            e01 = fp8_dec_scaled(xe, cs, false); e23 = fp8_dec_scaled(xe, cs, true);
+            o01 = fp8_dec_scaled(xo, cs, false); o23 = fp8_dec_scaled(xo, cs, true);
+        }
+        const float c[8] = {e01.x, o01.x, e01.y, o01.y, e23.x, o23.x, e23.y, o23.y};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (FIRST) acc[8 * d + j] = cs[j] * s9;
-            else acc[8 * d + j] = __builtin_fmaf(cs[j], s9, acc[8 * d + j]);
+            if (FIRST) acc[8 * d + j] = c[j] * m;
+            else acc[8 * d + j] = __builtin_fmaf(c[j], m, acc[8 * d + j]);
         }
     }
 }
 
 // ------------------------------------------------------------------ FP8 ----
-// Byte e of the block's 32 code bytes = E4M3 code of element e.
+// Byte e of the lane's 32 code bytes = E4M3 or E5M2 code of element e;
+// word d holds elements 4d..4d+3.
 
-struct Fp8Words { uint32_t d[8]; float s; };
+template <int FMT>
+__device__ __forceinline__ uint32_t f8_pair(float a, float b, uint32_t old, bool hi)
+{
+    if constexpr (FMT == 5) return bf8_pair(a, b, old, hi);
+    else return fp8_pair(a, b, old, hi);
+}
+
+template <int FMT>
+__device__ __forceinline__ f2 f8_dec(uint32_t w, bool hi)
+{
+    if constexpr (FMT == 5) return bf8_dec(w, hi);
+    else return fp8_dec(w, hi);
+}
 
 // Round-to-odd binary32 value of the exact quotient |x| / s, with the sign
-// of x and clamped to 448; its round-to-nearest-even E4M3 conversion equals
-// that of the exact quotient (binary32 carries more than 4 + 2 significant
-// bits).  rs is the hardware reciprocal of s (within 1 ulp):
+// of x and clamped to FMAX; its round-to-nearest-even conversion to E4M3 or
+// E5M2 equals that of the exact quotient (binary32 carries more than 4 + 2
+// significant bits).  rs is the hardware reciprocal of s (within 1 ulp):
 //   y0 = |x| * rs is within 3 ulp of the quotient q,
 //   y1 = y0 + fma(-y0, s, |x|) * rs is within 1/2 ulp (plus 2^-20 ulp) of q,
 //   and the sign of r = fma(-y1, s, |x|) (zero only when y1 = q) says on
 //   which side of y1 the quotient lies.
 // The residuals must not underflow: callers pass s >= 2^-64 (smaller block
 // scales are handled by multiplying x and s by 2^64).
+template <int FMAX>
 __device__ __forceinline__ float fp8_ro_quotient(float x, float s, float rs)
 {
     const float ax = fabsf(x);
@@ -365,50 +546,88 @@ __device__ __forceinline__ float fp8_ro_quotient(float x, float s, float rs)
     const float r = __builtin_fmaf(-y1, s, ax);
     uint32_t t = __float_as_uint(y1);
     t = (t - (r < 0.0f ? 1u : 0u)) | (r != 0.0f ? 1u : 0u);
-    const float yo = fminf(__uint_as_float(t), 448.0f);
+    const float yo = fminf(__uint_as_float(t), (float)FMAX);
     return __uint_as_float(__float_as_uint(yo) | (__float_as_uint(x) & 0x80000000u));
 }
 
-__device__ __forceinline__ void fp8_codes(const float (&v)[32], float k, float sk, uint32_t (&d)[8])
+// Codes of the exact quotients x / s (scales as multipliers m = s), with x
+// and s both multiplied by k (an exact power of two).
+template <int FMT, int H>
+__device__ __forceinline__ void fp8_quotient_codes(const float (&v)[32], const float (&sk)[H], float k,
+                                                   uint32_t (&d)[8])
 {
-    const float rs = __builtin_amdgcn_rcpf(sk);
+    float rs[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) rs[h] = __builtin_amdgcn_rcpf(sk[h]);
+    constexpr int FM = Fmt<FMT>::fmax;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        const int h = H == 2 ? i / 4 : 0;
         const float* x = v + 4 * i;
-        uint32_t w = fp8_pair(fp8_ro_quotient(x[0] * k, sk, rs), fp8_ro_quotient(x[1] * k, sk, rs), 0u, false);
-        d[i] = fp8_pair(fp8_ro_quotient(x[2] * k, sk, rs), fp8_ro_quotient(x[3] * k, sk, rs), w, true);
+        const uint32_t w = f8_pair<FMT>(fp8_ro_quotient<FM>(x[0] * k, sk[h], rs[h]),
+                                        fp8_ro_quotient<FM>(x[1] * k, sk[h], rs[h]), 0u, false);
+        d[i] = f8_pair<FMT>(fp8_ro_quotient<FM>(x[2] * k, sk[h], rs[h]),
+                            fp8_ro_quotient<FM>(x[3] * k, sk[h], rs[h]), w, true);
     }
 }
 
-__device__ __forceinline__ Fp8Words fp8_encode_block(const float (&v)[32])
+// FP8 codes (E4M3 / E5M2): with an FP32 or FP16 scale the exact-quotient
+// rounding above; with an E8M0 scale x * 2^-e is exact, clamped to the
+// format's largest magnitude and converted (RNE).
+template <int FMT, int SC, int H>
+__device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale (&sc)[H], uint32_t (&d)[8])
 {
-    Fp8Words o;
-    const float a = absmax32(v);
-    const float s = (a == __builtin_inff()) ? a : div_by<448>(a);   // inf / 448 = inf
-    const bool zero = !(s >= 0x1p-126f);
-    o.s = zero ? 0.0f : s;
-    if (!(s < 0x1p-64f)) {
-        fp8_codes(v, 1.0f, s, o.d);
-    } else {                                  // tiny scale: x * 2^64 and s * 2^64 are exact
-        fp8_codes(v, 0x1p64f, s * 0x1p64f, o.d);
-    }
+    constexpr float FM = (float)Fmt<FMT>::fmax;
+    if constexpr (SC == kSE8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o.d[i] = zero ? 0u : o.d[i];
-    return o;
+        for (int i = 0; i < 8; ++i) {
+            const float m = sc[H == 2 ? i / 4 : 0].m;
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(v[4 * i + j] * m, -FM), FM);
+            d[i] = f8_pair<FMT>(y[2], y[3], f8_pair<FMT>(y[0], y[1], 0u, false), true);
+        }
+    } else {
+        float s[H];
+        bool tiny = false;
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            s[h] = sc[h].zero ? 1.0f : sc[h].m;
+            if constexpr (SC == kS32) tiny = tiny || (s[h] < 0x1p-64f);
+        }
+        if (!tiny) {
+            fp8_quotient_codes<FMT, H>(v, s, 1.0f, d);
+        } else {                              // tiny scale: x * 2^64 and s * 2^64 are exact
+            float sk[H];
+#pragma unroll
+            for (int h = 0; h < H; ++h) sk[h] = s[h] * 0x1p64f;
+            fp8_quotient_codes<FMT, H>(v, sk, 0x1p64f, d);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] &= keep_mask(sc, i / 4);
+    }
 }
 
-template <bool FIRST>
-__device__ __forceinline__ void fp8_accumulate(const uint32_t (&D)[8], float s, float (&acc)[32])
+// acc[e] (+)= code_e * S.  FP32 scale: RN32(code * s) then RN32(acc + d);
+// FP16 and E8M0 scales: code * S is exact, so one fma is the same.
+template <int FMT, int SC, bool FIRST, int H>
+__device__ __forceinline__ void fp8_accumulate(const uint32_t (&D)[8], const float (&dm)[H], float (&acc)[32])
 {
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-        const f2 lo = fp8_dec(D[d], false), hi = fp8_dec(D[d], true);
+        const float m = dm[H == 2 ? d / 4 : 0];
+        const f2 lo = f8_dec<FMT>(D[d], false), hi = f8_dec<FMT>(D[d], true);
         const float c[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float dv = __fmul_rn(c[j], s);                 // RN32(code * s)
-            if (FIRST) acc[4 * d + j] = dv;
-            else acc[4 * d + j] = __fadd_rn(acc[4 * d + j], dv);  // RN32(acc + d)
+            if constexpr (SC == kS32) {
+                const float dv = __fmul_rn(c[j], m);                 // RN32(code * s)
+                if (FIRST) acc[4 * d + j] = dv;
+                else acc[4 * d + j] = __fadd_rn(acc[4 * d + j], dv);  // RN32(acc + d)
+            } else {
+                if (FIRST) acc[4 * d + j] = c[j] * m;
+                else acc[4 * d + j] = __builtin_fmaf(c[j], m, acc[4 * d + j]);
+            }
         }
     }
 }
@@ -416,41 +635,25 @@ __device__ __forceinline__ void fp8_accumulate(const uint32_t (&D)[8], float s, 
 // ---------------------------------------------------------------- MXFP4 ----
 // Word d holds elements 8d..8d+7 (element 8d+j in nibble j), E2M1 codes.
 
-struct MxWords { uint32_t d[4]; uint32_t e8; };
-
-// floor(log2 a) of a positive finite binary32, subnormals included.
-__device__ __forceinline__ int ilog2f(float a)
+template <int H>
+__device__ __forceinline__ void mx_encode(const float (&v)[32], const EncScale (&sc)[H], uint32_t (&D)[4])
 {
-    const uint32_t b = __float_as_uint(a);
-    const int ef = (int)(b >> 23);
-    return ef ? ef - 127 : (31 - (int)__builtin_clz(b)) - 149;
-}
-
-__device__ __forceinline__ MxWords mx_encode_block(const float (&v)[32])
-{
-    MxWords o;
-    const float a = absmax32(v);
-    int e = (a == 0.0f) ? -127 : ilog2f(a) - 2;
-    e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    o.e8 = (uint32_t)(e + 127);
-    const float p = __builtin_ldexpf(1.0f, e);          // 2^e, subnormal for e < -126
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+        const float p = sc[H == 2 ? d / 2 : 0].m;         // 2^e as the conversion's scale operand
         uint32_t w = 0u;
 #pragma unroll
         for (int b = 0; b < 4; ++b) w = fp4_enc(w, v[8 * d + 2 * b], v[8 * d + 2 * b + 1], p, b);
-        o.d[d] = w;
+        D[d] = w;
     }
-    return o;
 }
 
-template <bool FIRST>
-__device__ __forceinline__ void mx_accumulate(const uint32_t (&D)[4], uint32_t e8, float (&acc)[32])
+template <bool FIRST, int H>
+__device__ __forceinline__ void mx_accumulate(const uint32_t (&D)[4], const float (&dm)[H], float (&acc)[32])
 {
-    // 2^(e8-127) (subnormal below 2^-126); the E8M0 NaN byte makes every product NaN
-    const float p = (e8 == 255u) ? __builtin_nanf("") : __builtin_ldexpf(1.0f, (int)e8 - 127);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+        const float p = dm[H == 2 ? d / 2 : 0];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const f2 c = fp4_dec(D[d], 1.0f, b);            // code value, exact
@@ -460,6 +663,34 @@ __device__ __forceinline__ void mx_accumulate(const uint32_t (&D)[4], uint32_t e
                 acc[8 * d + 2 * b + 1] = __builtin_fmaf(c.y, p, acc[8 * d + 2 * b + 1]);
             }
         }
+    }
+}
+
+// ------------------------------------------------------ decode scales ----
+
+// E8M0 byte -> 2^(byte - 127 + k); the NaN byte makes every product NaN.
+template <int K>
+__device__ __forceinline__ float e8m0_mult(uint32_t b)
+{
+    return (b == 255u) ? __builtin_nanf("") : __builtin_ldexpf(1.0f, (int)b - 127 + K);
+}
+
+// Decode multiplier of one block from its stored scale bits: what the
+// format's code value (as the conversion instructions return it) is
+// multiplied by.
+template <int FMT, int SC>
+__device__ __forceinline__ float dec_mult(uint32_t bits)
+{
+    if constexpr (SC == kS16) {
+        const float s = __half2float(__ushort_as_half((unsigned short)bits));
+        if constexpr (FMT == 2) return 2.0f * s;          // E2M1 value q/2
+        else if constexpr (FMT == 1) return 512.0f * s;   // E4M3 subnormal q 2^-9
+        else return s;
+    } else if constexpr (SC == kS32) {
+        return __uint_as_float(bits);
+    } else {
+        if constexpr (FMT == 2) return e8m0_mult<1>(bits);
+        else return e8m0_mult<0>(bits);                   // INT4: codes decoded as q (scale operand 512)
     }
 }
 

@@ -1,0 +1,588 @@
+// rc_kernels.hpp -- kernel templates of the codec and their launcher
+// templates, for every (element format, scale type, block size).  Included
+// only by the instantiation units (rc_inst_*.hip); everything else sees the
+// launcher declarations of rc_launch.hpp.
+//
+// One wave64 per 2048-element tile, lane l = elements 32l..32l+31;
+// 256-thread workgroups (four waves).  Packed tiles are read and written with
+// per-lane buffer accesses that are contiguous across the wave (code words at
+// lane * bytes per 32 elements, scales at lane * scale bytes per lane); the
+// 64- or 128-byte element rows of quantize input and unpack output are
+// regrouped through LDS so that HBM sees wave-coalesced 16-byte chunks.
+#pragma once
+
+#include "rc_device.hpp"
+#include "rc_launch.hpp"
+
+#ifndef RC_GROUPS_PER_CU
+#define RC_GROUPS_PER_CU 256                       // grid cap, workgroups per CU
+#endif
+#ifndef RC_REDUCE_WAVES
+#define RC_REDUCE_WAVES 8                          // reduce occupancy target (waves per SIMD), INT / MX
+#endif
+#ifndef RC_REDUCE_BATCH
+#define RC_REDUCE_BATCH 2                          // streams loaded together, INT / MX
+#endif
+#ifndef RC_FP8_REDUCE_BATCH
+#define RC_FP8_REDUCE_BATCH 4                      // streams loaded together, FP8
+#endif
+#ifndef RC_FP8_REDUCE_WAVES
+#define RC_FP8_REDUCE_WAVES 4                      // reduce occupancy target, FP8
+#endif
+#ifndef RC_REDUCE_SCHED_BARRIER
+#define RC_REDUCE_SCHED_BARRIER 1                  // keep each batch's loads below the previous batch
+#endif
+#ifndef RC_QUANT_WAVES
+#define RC_QUANT_WAVES 8                           // quantize occupancy target, waves per SIMD
+#endif
+#ifndef RC_QUANT_LDS
+#define RC_QUANT_LDS 1                             // quantize input regrouped through LDS
+#endif
+#ifndef RC_UNPACK_LDS
+#define RC_UNPACK_LDS 1                            // unpack output regrouped through LDS
+#endif
+
+namespace rc {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Per-lane code words of 32 elements of one stream (scales load separately).
+template <int FMT> struct LaneCodes;
+template <> struct LaneCodes<kInt3> { uint32_t w0, w1, h; };
+template <> struct LaneCodes<kInt4> { uint32_t d[4]; };
+template <> struct LaneCodes<kFp8> { uint32_t d[8]; };
+template <> struct LaneCodes<kBf8> { uint32_t d[8]; };
+template <> struct LaneCodes<kMx4> { uint32_t d[4]; };
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------ buffer access ----
+// Tiles are addressed through a buffer descriptor built in scalar registers
+// from the (wave-uniform) tile address, and a per-lane byte offset that
+// does not change from tile to tile: no per-lane 64-bit address arithmetic.
+// Loads and stores carry the non-temporal hint.
+
+constexpr int kNT = 2;                              // aux bits: nt
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc span_rsrc(const void* base, size_t off, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const uint8_t*>(base) + off), (short)0,
+                                             (int)bytes, 0x00020000);
+}
+
+// The per-lane code words of 32 elements, read from a stream's tile.
+template <int FMT>
+__device__ __forceinline__ LaneCodes<FMT> load_codes_buf(Rsrc r, uint32_t lane)
+{
+    LaneCodes<FMT> c;
+    if constexpr (FMT == kInt3) {
+        const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8u, 0, kNT);
+        c.w0 = q.x;
+        c.w1 = q.y;
+        c.h = __builtin_amdgcn_raw_buffer_load_b32(r, 512u + lane * 4u, 0, kNT);
+    } else if constexpr (FMT == kFp8 || FMT == kBf8) {
+        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 32u, 0, kNT);
+        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 32u + 16u, 0, kNT);
+        c.d[0] = d0.x; c.d[1] = d0.y; c.d[2] = d0.z; c.d[3] = d0.w;
+        c.d[4] = d1.x; c.d[5] = d1.y; c.d[6] = d1.z; c.d[7] = d1.w;
+    } else {
+        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, kNT);
+        c.d[0] = d.x; c.d[1] = d.y; c.d[2] = d.z; c.d[3] = d.w;
+    }
+    return c;
+}
+
+// Raw scale bits of the lane's blocks: one scale (32-element blocks), two
+// adjacent scales (16), or the pair's shared scale (64), read at the
+// scale region's offset.
+template <int FMT, int SC, int BL>
+__device__ __forceinline__ void load_scale_bits(Rsrc r, uint32_t lane, uint32_t (&bits)[Halves<BL>::v])
+{
+    constexpr uint32_t base = Fmt<FMT>::code_bytes;
+    constexpr uint32_t SB = ScaleBytes<SC>::v;
+    if constexpr (BL == 16) {
+        if constexpr (SB == 2) {
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, base + lane * 4u, 0, kNT);
+            bits[0] = w & 0xFFFFu; bits[1] = w >> 16;
+        } else if constexpr (SB == 4) {
+            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, base + lane * 8u, 0, kNT);
+            bits[0] = w.x; bits[1] = w.y;
+        } else {
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b16(r, base + lane * 2u, 0, kNT);
+            bits[0] = w & 0xFFu; bits[1] = w >> 8;
+        }
+    } else {
+        const uint32_t idx = (BL == 64) ? (lane >> 1) : lane;
+        if constexpr (SB == 2) bits[0] = __builtin_amdgcn_raw_buffer_load_b16(r, base + idx * 2u, 0, kNT);
+        else if constexpr (SB == 4) bits[0] = __builtin_amdgcn_raw_buffer_load_b32(r, base + idx * 4u, 0, kNT);
+        else bits[0] = __builtin_amdgcn_raw_buffer_load_b8(r, base + idx, 0, kNT);
+    }
+}
+
+// Codes and decode multipliers of 32 elements of one stream.
+template <int FMT, int SC, int BL>
+struct LaneBlock {
+    LaneCodes<FMT> c;
+    uint32_t sbits[Halves<BL>::v];
+};
+
+template <int FMT, int SC, int BL>
+__device__ __forceinline__ LaneBlock<FMT, SC, BL> load_lane_block(Rsrc r, uint32_t lane)
+{
+    LaneBlock<FMT, SC, BL> b;
+    b.c = load_codes_buf<FMT>(r, lane);
+    load_scale_bits<FMT, SC, BL>(r, lane, b.sbits);
+    return b;
+}
+
+// acc (+)= decoded values of the lane's 32 elements.
+template <int FMT, int SC, int BL, bool FIRST>
+__device__ __forceinline__ void accumulate(const LaneBlock<FMT, SC, BL>& b, float (&acc)[32])
+{
+    constexpr int H = Halves<BL>::v;
+    float dm[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) dm[h] = dec_mult<FMT, SC>(b.sbits[h]);
+    if constexpr (FMT == kInt3) {
+        int3_accumulate<FIRST, H>(b.c.w0, b.c.w1, b.c.h, dm, acc);
+    } else if constexpr (FMT == kInt4) {
+        int4_accumulate<FIRST, H>(b.c.d, SC == kSE8 ? 512.0f : 1.0f, dm, acc);
+    } else if constexpr (FMT == kFp8 || FMT == kBf8) {
+        fp8_accumulate<FMT, SC, FIRST, H>(b.c.d, dm, acc);
+    } else {
+        mx_accumulate<FIRST, H>(b.c.d, dm, acc);
+    }
+}
+
+// Quantize the lane's 32 values and store its code words and scale(s).
+template <int FMT, int SC, int BL>
+__device__ __forceinline__ void encode_store_buf(const float (&v)[32], Rsrc r, uint32_t lane)
+{
+    constexpr int H = Halves<BL>::v;
+    float a[H];
+    lane_absmax<BL>(v, a);
+    EncScale sc[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) sc[h] = enc_scale<FMT, SC>(a[h]);
+    if constexpr (FMT == kInt3) {
+        const Int3Words w = int3_encode<H>(v, sc);
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){w.w0, w.w1}, r, lane * 8u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b32(w.h, r, 512u + lane * 4u, 0, kNT);
+    } else if constexpr (FMT == kInt4) {
+        uint32_t D[4];
+        int4_encode<H>(v, sc, D);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){D[0], D[1], D[2], D[3]}, r, lane * 16u, 0, kNT);
+    } else if constexpr (FMT == kFp8 || FMT == kBf8) {
+        uint32_t d[8];
+        fp8_encode<FMT, SC, H>(v, sc, d);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){d[0], d[1], d[2], d[3]}, r, lane * 32u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){d[4], d[5], d[6], d[7]}, r, lane * 32u + 16u, 0, kNT);
+    } else {
+        uint32_t D[4];
+        mx_encode<H>(v, sc, D);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){D[0], D[1], D[2], D[3]}, r, lane * 16u, 0, kNT);
+    }
+    constexpr uint32_t base = Fmt<FMT>::code_bytes;
+    constexpr uint32_t SB = ScaleBytes<SC>::v;
+    if constexpr (BL == 16) {
+        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b32(sc[0].bits | (sc[1].bits << 16), r, base + lane * 4u, 0, kNT);
+        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b64((u32x2){sc[0].bits, sc[1].bits}, r, base + lane * 8u, 0, kNT);
+        else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(sc[0].bits | (sc[1].bits << 8)), r, base + lane * 2u, 0, kNT);
+    } else if constexpr (BL == 32) {
+        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sc[0].bits, r, base + lane * 2u, 0, kNT);
+        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b32(sc[0].bits, r, base + lane * 4u, 0, kNT);
+        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc[0].bits, r, base + lane, 0, kNT);
+    } else if ((lane & 1u) == 0u) {                  // 64: the even lane of the pair stores
+        const uint32_t idx = lane >> 1;
+        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sc[0].bits, r, base + idx * 2u, 0, kNT);
+        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b32(sc[0].bits, r, base + idx * 4u, 0, kNT);
+        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc[0].bits, r, base + idx, 0, kNT);
+    }
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void tail_zero(float (&acc)[32], size_t base, size_t n)
+{
+    const size_t valid = (base >= n) ? 0 : n - base;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+        if ((size_t)e >= valid) acc[e] = 0.0f;
+}
+
+__device__ __forceinline__ void store_sums_tail(float* __restrict__ sum_out, size_t base, size_t n, const float (&acc)[32])
+{
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+        if (base + e < n) sum_out[base + e] = acc[e];
+}
+
+// ------------------------------------------------------------ kernels ----
+
+// Tile walk: each wave processes tiles first, first + stride, ...; `first`
+// and `stride` are wave-uniform (scalar registers), so tile addresses and
+// buffer descriptors are built with scalar arithmetic.
+struct TileWalk {
+    size_t first, stride;
+    int lane, w;
+};
+
+__device__ __forceinline__ TileWalk tile_walk()
+{
+    TileWalk t;
+    t.w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    t.lane = lane_id();
+    t.first = (size_t)blockIdx.x * kWavesPerGroup + (size_t)t.w;
+    t.stride = (size_t)gridDim.x * kWavesPerGroup;
+    return t;
+}
+
+// The 32 input elements of lane's block from the CPB 16-byte chunks of its
+// row, widened exactly to binary32.
+template <int DT, int CPB>
+__device__ __forceinline__ void widen_chunks(const u32x4 (&c)[CPB], float (&v)[32])
+{
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[4 * i] = __uint_as_float(c[i].x); v[4 * i + 1] = __uint_as_float(c[i].y);
+            v[4 * i + 2] = __uint_as_float(c[i].z); v[4 * i + 3] = __uint_as_float(c[i].w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) widen8<DT>(c[i], v + 8 * i);
+    }
+}
+
+// One wave quantizes one whole tile per iteration (fp32 input: the padded
+// LDS rows of four waves take 36 KiB, so at most 4 waves per SIMD fit).
+// With RC_QUANT_LDS the
+// tile's input is read as wave-coalesced 16-byte chunks (chunk c by lane
+// c % 64) and regrouped through a padded LDS row per lane; otherwise each
+// lane reads its own 16-byte chunks directly.  Codes and scales go out
+// through buffer stores.  Latency is covered by the other waves of the SIMD
+// (no in-wave prefetch).  The partial last tile, if any, is done after the
+// loop by the wave whose walk would reach it.
+template <int FMT, int SC, int BL, int DT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 ? 4 : RC_QUANT_WAVES)))
+void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict__ out, size_t tiles)
+{
+    constexpr int ES = (DT == kF32) ? 4 : 2;
+    constexpr int TIB = kTile * ES;            // input bytes of one tile
+    constexpr int BB = 32 * ES;                // input bytes of one lane
+    constexpr int CPB = BB / 16;               // 16-byte chunks per lane
+    constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
+    const TileWalk tw = tile_walk();
+    const uint32_t lane = (uint32_t)tw.lane;
+    const size_t full = n / kTile;
+#if RC_QUANT_LDS
+    constexpr int ROW = BB + 16;               // padded LDS row: conflict-free 16-byte reads
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    uint8_t* lds = sm[tw.w];
+#endif
+    for (size_t tile = tw.first; tile < full; tile += tw.stride) {
+        const Rsrc src = span_rsrc(in, tile * TIB, TIB);
+        u32x4 c[CPB];
+        float v[32];
+#if RC_QUANT_LDS
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (64u * i + lane) * 16u, 0, kNT);
+        wave_lds_sync();                       // the previous tile's rows are fully read
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) {
+            const uint32_t ch = 64u * i + lane;
+            *reinterpret_cast<u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16) = c[i];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) c[i] = *reinterpret_cast<const u32x4*>(lds + lane * ROW + 16 * i);
+#else
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, lane * BB + 16u * i, 0, kNT);
+#endif
+        widen_chunks<DT, CPB>(c, v);
+        encode_store_buf<FMT, SC, BL>(v, span_rsrc(out, tile * TB, TB), lane);
+    }
+    if (full != tiles && full % tw.stride == tw.first) {     // the partial last tile
+        float v[32];
+        load_block<DT>(in, full * kTile + (size_t)lane * 32, n, v);
+        encode_store_buf<FMT, SC, BL>(v, span_rsrc(out, full * TB, TB), lane);
+    }
+}
+
+// Streams whose codes are loaded together before they are accumulated.
+// FP8's encoder holds more registers: it runs at fewer waves per SIMD.
+template <int FMT> struct ReduceBatch {
+    static constexpr int v = (FMT == kFp8 || FMT == kBf8) ? RC_FP8_REDUCE_BATCH : RC_REDUCE_BATCH;
+};
+template <int FMT> struct ReduceWaves {
+    static constexpr int v = (FMT == kFp8 || FMT == kBf8) ? RC_FP8_REDUCE_WAVES : RC_REDUCE_WAVES;
+};
+
+// acc = the K streams' decoded values of the lane's 32 elements of `tile`,
+// added in stream order in binary32.  K > 0: K known at compile time, loads
+// in batches; K == 0: k streams at run time, loads two at a time.
+template <int FMT, int SC, int BL, int K>
+__device__ __forceinline__ void reduce_tile(const StreamPtrs& ins, int k, size_t tile, uint32_t lane, float (&acc)[32])
+{
+    constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
+    if constexpr (K > 0) {
+        constexpr int B = (K < ReduceBatch<FMT>::v) ? K : ReduceBatch<FMT>::v;
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += B) {
+            LaneBlock<FMT, SC, BL> c[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                if (k0 + j < K) c[j] = load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[k0 + j], tile * TB, TB), lane);
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (k0 + j >= K) break;
+                if (k0 + j == 0) accumulate<FMT, SC, BL, true>(c[j], acc);
+                else accumulate<FMT, SC, BL, false>(c[j], acc);
+            }
+            // keep the next batch's loads below this batch's arithmetic (bounds
+            // the registers held by codes in flight)
+            if (RC_REDUCE_SCHED_BARRIER && k0 + B < K) __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[0], tile * TB, TB), lane), acc);
+        int j = 1;
+        for (; j + 1 < k; j += 2) {
+            const LaneBlock<FMT, SC, BL> c0 = load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j], tile * TB, TB), lane);
+            const LaneBlock<FMT, SC, BL> c1 = load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j + 1], tile * TB, TB), lane);
+            accumulate<FMT, SC, BL, false>(c0, acc);
+            accumulate<FMT, SC, BL, false>(c1, acc);
+        }
+        if (j < k)
+            accumulate<FMT, SC, BL, false>(load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j], tile * TB, TB), lane), acc);
+    }
+}
+
+__device__ __forceinline__ void store_sums(float* __restrict__ sum_out, size_t tile, uint32_t lane, const float (&acc)[32])
+{
+    const Rsrc r = span_rsrc(sum_out, tile * (kTile * 4), kTile * 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){__float_as_uint(acc[4 * i]), __float_as_uint(acc[4 * i + 1]),
+                                                       __float_as_uint(acc[4 * i + 2]), __float_as_uint(acc[4 * i + 3])},
+                                               r, lane * 128u + 16u * i, 0, kNT);
+}
+
+// Each wave reduces whole tiles: the codes of the K streams are read with
+// per-lane coalesced loads, decoded and accumulated in registers, and the
+// sums requantized in place.  No LDS and no in-wave prefetch: latency is
+// covered by the other waves of the SIMD.  The partial last tile (if any)
+// is done after the loop by the wave whose walk would reach it.
+template <int FMT, int SC, int BL, int K>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ReduceWaves<FMT>::v)))
+void reduce_kernel(StreamPtrs ins, int k, size_t n, uint8_t* __restrict__ out, float* __restrict__ sum_out,
+                   size_t tiles)
+{
+    constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
+    const TileWalk tw = tile_walk();
+    const uint32_t lane = (uint32_t)tw.lane;
+    const size_t full = n / kTile;
+    if (sum_out) {
+        for (size_t tile = tw.first; tile < full; tile += tw.stride) {
+            float acc[32];
+            reduce_tile<FMT, SC, BL, K>(ins, k, tile, lane, acc);
+            store_sums(sum_out, tile, lane, acc);
+            encode_store_buf<FMT, SC, BL>(acc, span_rsrc(out, tile * TB, TB), lane);
+        }
+    } else {
+        for (size_t tile = tw.first; tile < full; tile += tw.stride) {
+            float acc[32];
+            reduce_tile<FMT, SC, BL, K>(ins, k, tile, lane, acc);
+            encode_store_buf<FMT, SC, BL>(acc, span_rsrc(out, tile * TB, TB), lane);
+        }
+    }
+    if (full != tiles && full % tw.stride == tw.first) {
+        float acc[32];
+        reduce_tile<FMT, SC, BL, K>(ins, k, full, lane, acc);
+        const size_t base = full * kTile + (size_t)lane * 32;
+        tail_zero(acc, base, n);                   // positions >= n are +0
+        if (sum_out) store_sums_tail(sum_out, base, n, acc);
+        encode_store_buf<FMT, SC, BL>(acc, span_rsrc(out, full * TB, TB), lane);
+    }
+}
+
+// binary32 -> binary16 bits, RNE.  The empty asm pins x in a register so the
+// compiler cannot fold the producing multiply into the conversion (an fma
+// into f16 with a +0 addend would turn -0 products into +0).
+__device__ __forceinline__ uint32_t f16_bits(float x)
+{
+    __asm__("" : "+v"(x));
+    return __half_as_ushort(__float2half_rn(x));
+}
+
+// The 32 decoded values of one block as output words (16 for 2-byte dtypes).
+template <int ODT>
+__device__ __forceinline__ void out_words(const float (&d)[32], uint32_t (&w)[32])
+{
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        if constexpr (ODT == kF32) w[i] = __float_as_uint(d[i]);
+        else if (i < 16) {
+            if constexpr (ODT == kBF16) {
+                __hip_bfloat162 b = __float22bfloat162_rn(make_float2(d[2 * i], d[2 * i + 1]));
+                w[i] = *reinterpret_cast<uint32_t*>(&b);
+            } else {
+                w[i] = f16_bits(d[2 * i]) | (f16_bits(d[2 * i + 1]) << 16);
+            }
+        }
+    }
+}
+
+template <int ODT>
+__device__ __forceinline__ void store_block_guarded(void* __restrict__ out, size_t base, size_t n, const float (&d)[32])
+{
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        if (base + e >= n) continue;
+        if constexpr (ODT == kF32) static_cast<float*>(out)[base + e] = d[e];
+        else if constexpr (ODT == kBF16)
+            static_cast<uint16_t*>(out)[base + e] = __bfloat16_as_ushort(__float2bfloat16(d[e]));
+        else static_cast<uint16_t*>(out)[base + e] = (uint16_t)f16_bits(d[e]);
+    }
+}
+
+// One wave unpacks one tile per iteration: codes in through per-lane buffer
+// loads, decoded values out either through a padded LDS row per lane and
+// wave-coalesced 16-byte stores (RC_UNPACK_LDS) or straight from each lane.
+template <int FMT, int SC, int BL, int ODT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ODT == kF32 ? 4 : 8)))
+void unpack_kernel(const uint8_t* __restrict__ in, size_t n, void* __restrict__ out, size_t tiles)
+{
+    constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
+    constexpr int ES = (ODT == kF32) ? 4 : 2;
+    constexpr int OB = 32 * ES;                // output bytes of one lane
+    constexpr int CPB = OB / 16;
+    const TileWalk tw = tile_walk();
+    const uint32_t lane = (uint32_t)tw.lane;
+    const size_t full = n / kTile;
+#if RC_UNPACK_LDS
+    constexpr int ROW = OB + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    uint8_t* lds = sm[tw.w];
+#endif
+    for (size_t tile = tw.first; tile < full; tile += tw.stride) {
+        float d[32];
+        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL>(span_rsrc(in, tile * TB, TB), lane), d);
+        uint32_t wd[32];
+        out_words<ODT>(d, wd);
+        const Rsrc dst = span_rsrc(out, tile * (size_t)(kTile * ES), kTile * ES);
+#if RC_UNPACK_LDS
+        wave_lds_sync();                       // the previous tile's rows are fully read
+#pragma unroll
+        for (int i = 0; i < CPB; ++i)
+            *reinterpret_cast<u32x4*>(lds + lane * ROW + 16 * i) =
+                (u32x4){wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]};
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) {
+            const uint32_t ch = 64u * i + lane;
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16),
+                                                   dst, ch * 16u, 0, kNT);
+        }
+#else
+#pragma unroll
+        for (int i = 0; i < CPB; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]},
+                                                   dst, lane * OB + 16u * i, 0, kNT);
+#endif
+    }
+    if (full != tiles && full % tw.stride == tw.first) {     // the partial last tile
+        float d[32];
+        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL>(span_rsrc(in, full * TB, TB), lane), d);
+        store_block_guarded<ODT>(out, full * kTile + (size_t)lane * 32, n, d);
+    }
+}
+
+// ---------------------------------------------------------- launchers ----
+
+// Grid of four-wave workgroups: one tile per wave up to RC_GROUPS_PER_CU
+// workgroups per compute unit (1 GiB of bf16 input on 256 CUs; measured
+// faster there than a 4x smaller grid walking 4 tiles per wave); beyond that
+// each wave walks several tiles.
+static inline dim3 tile_grid(size_t tiles)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const size_t groups = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+    const size_t cap = (size_t)RC_GROUPS_PER_CU * (size_t)(cus > 0 ? cus : 256);
+    return dim3((unsigned)(groups < cap ? groups : cap));
+}
+
+template <int FMT, int SC, int BL>
+hipError_t launch_quantize_t(int dt, const void* in, size_t n, void* out, hipStream_t st)
+{
+    const size_t tiles = (n + kTile - 1) / kTile;
+    uint8_t* o = static_cast<uint8_t*>(out);
+    switch (dt) {
+    case kF32: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF32>), tile_grid(tiles), dim3(256), 0, st, in, n, o, tiles); break;
+    case kF16: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF16>), tile_grid(tiles), dim3(256), 0, st, in, n, o, tiles); break;
+    default:   hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kBF16>), tile_grid(tiles), dim3(256), 0, st, in, n, o, tiles); break;
+    }
+    return hipGetLastError();
+}
+
+template <int FMT, int SC, int BL>
+hipError_t launch_unpack_t(const void* in, size_t n, int dt, void* out, hipStream_t st)
+{
+    const size_t tiles = (n + kTile - 1) / kTile;
+    const uint8_t* i = static_cast<const uint8_t*>(in);
+    switch (dt) {
+    case kF32: hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kF32>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break;
+    case kF16: hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kF16>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break;
+    default:   hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kBF16>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break;
+    }
+    return hipGetLastError();
+}
+
+template <int FMT, int SC, int BL, int K>
+static hipError_t launch_reduce_k(const StreamPtrs& p, int k, size_t n, void* out, float* sum, hipStream_t st)
+{
+    const size_t tiles = (n + kTile - 1) / kTile;
+    hipLaunchKernelGGL((reduce_kernel<FMT, SC, BL, K>), tile_grid(tiles), dim3(256), 0, st, p, k, n,
+                       static_cast<uint8_t*>(out), sum, tiles);
+    return hipGetLastError();
+}
+
+// Reduce with K unrolled at compile time (K = 1..16).
+template <int FMT, int SC, int BL>
+hipError_t launch_reduce_unrolled_t(const StreamPtrs& p, int k, size_t n, void* out, float* sum, hipStream_t st)
+{
+    switch (k) {
+    case 1:  return launch_reduce_k<FMT, SC, BL, 1>(p, k, n, out, sum, st);
+    case 2:  return launch_reduce_k<FMT, SC, BL, 2>(p, k, n, out, sum, st);
+    case 3:  return launch_reduce_k<FMT, SC, BL, 3>(p, k, n, out, sum, st);
+    case 4:  return launch_reduce_k<FMT, SC, BL, 4>(p, k, n, out, sum, st);
+    case 5:  return launch_reduce_k<FMT, SC, BL, 5>(p, k, n, out, sum, st);
+    case 6:  return launch_reduce_k<FMT, SC, BL, 6>(p, k, n, out, sum, st);
+    case 7:  return launch_reduce_k<FMT, SC, BL, 7>(p, k, n, out, sum, st);
+    case 8:  return launch_reduce_k<FMT, SC, BL, 8>(p, k, n, out, sum, st);
+    case 9:  return launch_reduce_k<FMT, SC, BL, 9>(p, k, n, out, sum, st);
+    case 10: return launch_reduce_k<FMT, SC, BL, 10>(p, k, n, out, sum, st);
+    case 11: return launch_reduce_k<FMT, SC, BL, 11>(p, k, n, out, sum, st);
+    case 12: return launch_reduce_k<FMT, SC, BL, 12>(p, k, n, out, sum, st);
+    case 13: return launch_reduce_k<FMT, SC, BL, 13>(p, k, n, out, sum, st);
+    case 14: return launch_reduce_k<FMT, SC, BL, 14>(p, k, n, out, sum, st);
+    case 15: return launch_reduce_k<FMT, SC, BL, 15>(p, k, n, out, sum, st);
+    default: return launch_reduce_k<FMT, SC, BL, 16>(p, k, n, out, sum, st);
+    }
+}
+
+// Reduce with the stream count a run-time loop (one kernel for every k).
+template <int FMT, int SC, int BL>
+hipError_t launch_reduce_rt_t(const StreamPtrs& p, int k, size_t n, void* out, float* sum, hipStream_t st)
+{
+    return launch_reduce_k<FMT, SC, BL, 0>(p, k, n, out, sum, st);
+}
+
+}  // namespace rc

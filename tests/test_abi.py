@@ -29,13 +29,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert rca.lib().rc_abi_version() == 1
+    assert rca.lib().rc_abi_version() == 2
 
 
 def test_enums_agree_with_oracle():
     src = open(HEADER).read()
     for key, val in [("RC_FMT_INT4", oracle.FMT_INT4), ("RC_FMT_INT3", oracle.FMT_INT3),
                      ("RC_FMT_FP8_E4M3", oracle.FMT_FP8_E4M3), ("RC_FMT_MXFP4", oracle.FMT_MXFP4),
+                     ("RC_FMT_FP8_E5M2", oracle.FMT_FP8_E5M2),
                      ("RC_SCALE_FP16", oracle.SCALE_FP16), ("RC_SCALE_FP32", oracle.SCALE_FP32),
                      ("RC_SCALE_E8M0", oracle.SCALE_E8M0), ("RC_DT_FP32", oracle.DT_FP32),
                      ("RC_DT_FP16", oracle.DT_FP16), ("RC_DT_BF16", oracle.DT_BF16),
@@ -54,9 +55,19 @@ def test_sizes_agree_with_oracle(name):
         assert rca.packed_bytes(c, n) == oracle.packed_bytes(oracle.CODECS[name], n)
 
 
+def test_codec_lists_agree_with_oracle():
+    assert sorted(rca.ALL_CODECS) == sorted(oracle.ALL_CODECS)
+    for name, c in rca.ALL_CODECS.items():
+        assert (c.format, c.scale, c.block) == oracle.ALL_CODECS[name]
+        assert rca.tile_bytes(c) == oracle.tile_bytes(oracle.ALL_CODECS[name]), name
+        assert rca.packed_bytes(c, 5 * 2048 + 7) == oracle.packed_bytes(oracle.ALL_CODECS[name], 5 * 2048 + 7)
+
+
 def test_unsupported_codecs_have_no_size():
-    for c in [(1, 2, 32), (2, 3, 32), (3, 1, 32), (4, 2, 32), (1, 1, 16), (5, 1, 32)]:
+    for c in [(1, 2, 32), (2, 2, 32), (4, 1, 32), (4, 2, 32), (1, 1, 8), (3, 2, 128), (5, 2, 48), (9, 1, 32),
+              (0, 3, 32)]:
         assert rca.lib().rc_tile_bytes(rca.Codec(*c)) == 0
+        assert oracle.tile_bytes(c) == 0
 
 
 A = 0x10000          # an aligned, non-null address that is never dereferenced
@@ -78,7 +89,8 @@ def st_r(codec, ptrs, k, n, out, sums=None):
 
 def test_quantize_error_paths():
     c = rca.INT3
-    assert st_q(rca.Codec(2, 1, 16), 3, A, 10, A) == rca.ERR_UNSUPPORTED
+    assert st_q(rca.Codec(2, 1, 8), 3, A, 10, A) == rca.ERR_UNSUPPORTED
+    assert st_q(rca.Codec(2, 2, 32), 3, A, 10, A) == rca.ERR_UNSUPPORTED
     assert st_q(rca.Codec(9, 1, 32), 3, A, 10, A) == rca.ERR_UNSUPPORTED
     assert st_q(c, 7, A, 10, A) == rca.ERR_UNSUPPORTED
     assert st_q(c, 3, None, 10, A) == rca.ERR_NULL
@@ -92,6 +104,7 @@ def test_quantize_error_paths():
 def test_unpack_error_paths():
     c = rca.MXFP4
     assert st_u(rca.Codec(4, 1, 32), A, 10, 1, A) == rca.ERR_UNSUPPORTED
+    assert st_u(rca.Codec(5, 2, 128), A, 10, 1, A) == rca.ERR_UNSUPPORTED
     assert st_u(c, A, 10, 0, A) == rca.ERR_UNSUPPORTED
     assert st_u(c, None, 10, 1, A) == rca.ERR_NULL
     assert st_u(c, A, 10, 1, None) == rca.ERR_NULL
@@ -102,7 +115,8 @@ def test_unpack_error_paths():
 
 def test_reduce_error_paths():
     c = rca.FP8
-    assert st_r(rca.Codec(3, 1, 32), [A], 1, 10, A) == rca.ERR_UNSUPPORTED
+    assert st_r(rca.Codec(3, 1, 48), [A], 1, 10, A) == rca.ERR_UNSUPPORTED
+    assert st_r(rca.Codec(4, 2, 32), [A], 1, 10, A) == rca.ERR_UNSUPPORTED
     assert st_r(c, [A], 0, 10, A) == rca.ERR_RANGE
     assert st_r(c, [A] * 17, 17, 10, A) == rca.ERR_RANGE
     assert st_r(c, None, 2, 10, A) == rca.ERR_NULL

@@ -365,3 +365,61 @@ def test_sweep_sampled_tiles(fmt, mib):
         assert np.array_equal(hout[t * tb:(t + 1) * tb], refo[t * tb:(t + 1) * tb]), f"reduce tile {t}"
     del dev_packed, out
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------- format / scale variants ----
+
+VARIANTS = sorted(rca.ALL_CODECS)
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+@pytest.mark.parametrize("dt", DTYPES)
+def test_variant_quantize_bit_exact(name, dt):
+    n = 2 * 2048 + 777
+    say(f"case variant quantize {name} dt={dt} n={n}")
+    x = mixed(n, seed=len(name) * 31 + n, dt=dt)
+    ref = oracle.quantize_pack(oracle.ALL_CODECS[name], x, dtype=ORACLE_DT[dt])
+    c = rca.ALL_CODECS[name]
+    pb = rca.packed_bytes(c, n)
+    buf = torch.full((pb + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    rca.quantize_pack(to_dev(x, dt), c, out=buf[:pb])
+    got = host_u8(buf)
+    assert_same(got[:pb], ref, name)
+    assert (got[pb:] == 0xA5).all(), "wrote past the packed size"
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+@pytest.mark.parametrize("odt", DTYPES)
+def test_variant_unpack_bit_exact(name, odt):
+    n = 2048 + 1000
+    say(f"case variant unpack {name} odt={odt}")
+    x = mixed(n, seed=7 + len(name), dt="fp32")
+    packed = oracle.quantize_pack(oracle.ALL_CODECS[name], x, dtype=oracle.DT_FP32)
+    ref = oracle.unpack_dequant(oracle.ALL_CODECS[name], packed, n, ORACLE_DT[odt])
+    got = rca.unpack_dequant(torch.from_numpy(packed).to(DEV), rca.ALL_CODECS[name], n, TORCH_DT[odt])
+    g = got.cpu()
+    g = g.view(torch.int16).numpy().view(np.uint16) if odt == "bf16" else g.numpy()
+    assert_same(g, ref, name)
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_variant_reduce_bit_exact(name, k):
+    n = 2 * 2048 + 300
+    say(f"case variant reduce {name} k={k}")
+    c_or = oracle.ALL_CODECS[name]
+    streams = []
+    for j in range(k):
+        x = mixed(n, 50 * k + 13 * j, "fp32") if j % 2 == 0 else \
+            (np.random.default_rng(j).standard_normal(n) * (j + 1)).astype(np.float32)
+        streams.append(oracle.quantize_pack(c_or, x, dtype=oracle.DT_FP32))
+    ref, ref_sum = oracle.dequant_reduce_requant(c_or, streams, n, want_sum=True)
+    c = rca.ALL_CODECS[name]
+    pb = rca.packed_bytes(c, n)
+    buf = torch.full((pb + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    _, sums = rca.dequant_reduce_requant([torch.from_numpy(s).to(DEV) for s in streams], c, n,
+                                         out=buf[:pb], sum_out=True)
+    got = host_u8(buf)
+    assert_same(got[:pb], ref, name)
+    assert (got[pb:] == 0xA5).all()
+    assert_sums(sums.cpu().numpy(), ref_sum)
