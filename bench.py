@@ -67,6 +67,8 @@ def parse_args():
     ap.add_argument("--table-codecs", default="int3,int4,fp8,mxfp4",
                     help="comma list of codec names (default names or <elem>_<scale>_b<block>), or 'all'")
     ap.add_argument("--table-k", default="2,4,8", help="stream counts of the reduce rows")
+    ap.add_argument("--fused", action="store_true",
+                    help="fused all-reduce emulation against the separate kernels (no JSON line)")
     return ap.parse_args()
 
 
@@ -154,6 +156,8 @@ def main():
         return summarize_trace(args.summarize_trace)
     if args.table:
         return table(args)
+    if args.fused:
+        return fused_table(args)
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU only: this codec build has no multi-GPU path "
                          "(run with --gpus 1)\n")
@@ -365,6 +369,74 @@ def table(args):
                 print(f"| {mib} | {fmt} | {name} | {ms * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
                       f"{unc / (ms * 1e-3) / 1e9:.0f} |", flush=True)
             del bufs
+            torch.cuda.empty_cache()
+    return 0
+
+
+def fused_table(args):
+    """The fused one-GPU all-reduce emulation (rc_allreduce_emulate, two-shot
+    and one-shot) against the same pipeline as separate kernels (K quantizes,
+    one K-stream reduce, one unpack), for bf16 messages of --table-mib MiB
+    per emulated rank.  HBM bytes count what each variant must move: fused =
+    K messages in + output (+ the packed sum for two-shot); separate = every
+    kernel's inputs and outputs."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import reduction_codec_amd as rca
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def timed(fn, reps=20):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    print("| MiB/rank | codec | K | variant | us | HBM GB/s | % of peak | uncompressed GB/s | vs separate |")
+    print("|---:|---|---:|---|---:|---:|---:|---:|---:|")
+    for mib in [int(v) for v in args.table_mib.split(",")]:
+        n = mib * (1 << 20) // 2
+        for K in [int(v) for v in args.table_k.split(",")]:
+            msgs = [torch.from_numpy(datagen.bf16_student4(2 * n, 500 + j).view(np.int16)).view(torch.bfloat16).to(dev)
+                    for j in range(K)]
+            for fmt in ("int3", "int4", "fp8", "mxfp4"):
+                c = rca.CODECS[fmt]
+                pb = rca.packed_bytes(c, n)
+                out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+                packed = torch.empty(pb, dtype=torch.uint8, device=dev)
+                streams = [torch.empty(pb, dtype=torch.uint8, device=dev) for _ in range(K)]
+
+                def separate(i):
+                    for j in range(K):
+                        rca.quantize_pack(msgs[j], c, out=streams[j])
+                    rca.dequant_reduce_requant(streams, c, n, out=packed)
+                    rca.unpack_dequant(packed, c, n, torch.bfloat16, out=out)
+
+                t_sep = timed(separate)
+                b_sep = K * (2 * n + pb) + (K + 1) * pb + (pb + 2 * n)
+                t2 = timed(lambda i: rca.allreduce_emulate(msgs, c, True, out=out, packed_out=packed))
+                t1 = timed(lambda i: rca.allreduce_emulate(msgs, c, False, out=out))
+                unc = K * 2 * n
+                for name, t, b in (("separate kernels", t_sep, b_sep), ("fused two-shot", t2, K * 2 * n + 2 * n + pb),
+                                   ("fused one-shot", t1, K * 2 * n + 2 * n)):
+                    g = b / (t * 1e-3) / 1e9
+                    print(f"| {mib} | {fmt} | {K} | {name} | {t * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
+                          f"{unc / (t * 1e-3) / 1e9:.0f} | {t_sep / t:.2f}x |", flush=True)
+                del streams, out, packed
+            del msgs
             torch.cuda.empty_cache()
     return 0
 

@@ -131,6 +131,29 @@ rc_status rc_unpack_dequant(rc_codec c, const void *in, size_t n, rc_dtype out_t
 rc_status rc_dequant_reduce_requant(rc_codec c, const void *const *ins, int k, size_t n,
                                     void *out, float *sum_out, void *stream);
 
+/* Fused single-GPU emulation of a quantized all-reduce over k messages that
+ * all sit in this GPU's memory, one per emulated rank ("RCCLX: Innovating
+ * GPU communications on AMD platforms" -- Direct Data Access: the flat
+ * one-shot and the tree-shaped two-shot all-reduce, with the low-precision
+ * payloads of Low-Precision Collectives).  Every message is quantized with
+ * codec c and decoded (what a receiving rank decodes), the decoded values
+ * are added in FP32 in message order, and then
+ *   two_shot != 0 (reduce-scatter and all-gather both carry compressed data):
+ *     out = unpack_dequant(requantize(sum)), and the requantized sum (the
+ *     all-gather payload, rc_packed_bytes(c, n) bytes) goes to packed_out
+ *     when packed_out is not NULL;
+ *   two_shot == 0 (every rank reads all compressed messages):
+ *     out = the sum rounded to dt (RNE), packed_out unused.
+ * Exactly what the separate calls compute (rc_quantize_pack of each message,
+ * rc_dequant_reduce_requant with sums, rc_unpack_dequant), in one kernel
+ * pass that touches only the messages, out and packed_out.
+ *   msgs: host array of k device pointers to n elements of dt each;
+ *   out:  n elements of dt.  Default codecs only ({INT4, FP16, 32},
+ *   {INT3, FP16, 32}, {FP8_E4M3, FP32, 32}, {MXFP4, E8M0, 32}); others
+ *   return RC_ERR_UNSUPPORTED.  Errors as for rc_dequant_reduce_requant. */
+rc_status rc_allreduce_emulate(rc_codec c, rc_dtype dt, const void *const *msgs, int k, size_t n,
+                               int two_shot, void *out, void *packed_out, void *stream);
+
 /* Plain device-to-device copy of `bytes` bytes (multiple of 16) with the same
  * 16-byte vector loads/stores as the codec kernels: the bandwidth baseline
  * the codec kernels are measured against. */

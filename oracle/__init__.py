@@ -323,3 +323,21 @@ def fp8_scale_f16_bits(amax, fmt: int):
     out = np.empty(amax.size, dtype=np.uint16)
     _load().rco_map_fp8_scale_f16_bits(_ptr(amax), fmt, _ptr(out), amax.size)
     return out
+
+
+def allreduce_emulate(c, msgs, dtype: int, two_shot: bool = True):
+    """What a quantized all-reduce of the messages (one per rank) delivers,
+    composed from the operations above: quantize every message, reduce the
+    packed streams (FP32 sums in message order), then either unpack the
+    requantized sum (two-shot) or round the sums to the messages' dtype
+    (one-shot).  Returns (out, packed requantized sum)."""
+    n = msgs[0].size
+    streams = [quantize_pack(c, m, dtype=dtype) for m in msgs]
+    packed, sums = dequant_reduce_requant(c, streams, n, want_sum=True)
+    if two_shot:
+        return unpack_dequant(c, packed, n, dtype), packed
+    if dtype == DT_FP32:
+        return sums, packed
+    if dtype == DT_FP16:
+        return f32_to_f16_bits(sums).view(np.float16), packed
+    return f32_to_bf16_bits(sums), packed

@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     l.rc_dequant_reduce_requant.restype = i32
     l.rc_dequant_reduce_requant.argtypes = [Codec, ctypes.POINTER(vp), i32, sz, vp, vp, vp]
     l.rc_copy.restype, l.rc_copy.argtypes = i32, [vp, vp, sz, vp]
+    l.rc_allreduce_emulate.restype = i32
+    l.rc_allreduce_emulate.argtypes = [Codec, i32, ctypes.POINTER(vp), i32, sz, i32, vp, vp, vp]
     l.rc_status_str.restype, l.rc_status_str.argtypes = ctypes.c_char_p, [i32]
     l.rc_abi_version.restype, l.rc_abi_version.argtypes = i32, []
     _lib = l
@@ -198,6 +200,44 @@ def dequant_reduce_requant(streams, codec, n: int, out: torch.Tensor | None = No
                                         sums.data_ptr() if sums is not None else None, _stream(stream)),
         "rc_dequant_reduce_requant")
     return out, sums
+
+
+def allreduce_emulate(msgs, codec, two_shot: bool = True, out: torch.Tensor | None = None,
+                      packed_out: bool | torch.Tensor = False, stream=None):
+    """Fused one-GPU emulation of a quantized all-reduce of the messages (one
+    per emulated rank, same dtype and length).  Returns (out, packed or
+    None); see rc_allreduce_emulate in include/rcodec.h."""
+    c = _codec(codec)
+    msgs = list(msgs)
+    k = len(msgs)
+    if not 1 <= k <= MAX_STREAMS:
+        raise ValueError(f"need 1..{MAX_STREAMS} messages, got {k}")
+    dt = msgs[0].dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    n = msgs[0].numel()
+    for j, m in enumerate(msgs):
+        _check_dev(m, f"msgs[{j}]")
+        if m.dtype != dt or m.numel() != n:
+            raise ValueError("all messages need the same dtype and length")
+    if out is None:
+        out = torch.empty(n, dtype=dt, device=msgs[0].device)
+    _check_dev(out, "out")
+    if out.dtype != dt or out.numel() < n:
+        raise ValueError("out must hold n elements of the messages' dtype")
+    packed = None
+    if isinstance(packed_out, torch.Tensor):
+        packed = packed_out
+        _check_dev(packed, "packed_out")
+        if packed.numel() < packed_bytes(c, n) or packed.dtype != torch.uint8:
+            raise ValueError("packed_out must be a uint8 tensor of packed_bytes(codec, n) bytes")
+    elif packed_out:
+        packed = torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=msgs[0].device)
+    ptrs = (ctypes.c_void_p * k)(*[m.data_ptr() for m in msgs])
+    _ok(lib().rc_allreduce_emulate(c, _DTYPES[dt], ptrs, k, n, 1 if two_shot else 0, out.data_ptr(),
+                                   packed.data_ptr() if packed is not None else None, _stream(stream)),
+        "rc_allreduce_emulate")
+    return out, packed
 
 
 def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> torch.Tensor:

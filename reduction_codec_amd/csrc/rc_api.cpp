@@ -92,6 +92,30 @@ rc_status rc_dequant_reduce_requant(rc_codec c, const void* const* ins, int k, s
     return from_hip(rc::launch_reduce(c.format, c.scale, c.block, p, k, n, out, sum_out, static_cast<hipStream_t>(stream)));
 }
 
+rc_status rc_allreduce_emulate(rc_codec c, rc_dtype dt, const void* const* msgs, int k, size_t n, int two_shot,
+                               void* out, void* packed_out, void* stream)
+{
+    if (!codec_ok(c) || !dtype_ok(dt) || c.block != RC_BLOCK_ELEMS) return RC_ERR_UNSUPPORTED;
+    const bool dflt = (c.format == RC_FMT_INT4 && c.scale == RC_SCALE_FP16) ||
+                      (c.format == RC_FMT_INT3 && c.scale == RC_SCALE_FP16) ||
+                      (c.format == RC_FMT_FP8_E4M3 && c.scale == RC_SCALE_FP32) ||
+                      (c.format == RC_FMT_MXFP4 && c.scale == RC_SCALE_E8M0);
+    if (!dflt) return RC_ERR_UNSUPPORTED;
+    if (k < 1 || k > RC_MAX_STREAMS) return RC_ERR_RANGE;
+    if (n == 0) return RC_OK;
+    if (n > kMaxElems) return RC_ERR_RANGE;
+    if (!msgs || !out) return RC_ERR_NULL;
+    rc::StreamPtrs p = {};
+    for (int j = 0; j < k; ++j) {
+        if (!msgs[j]) return RC_ERR_NULL;
+        if (!aligned16(msgs[j])) return RC_ERR_ALIGN;
+        p.p[j] = static_cast<const uint8_t*>(msgs[j]);
+    }
+    if (!aligned16(out) || (packed_out && !aligned16(packed_out))) return RC_ERR_ALIGN;
+    return from_hip(rc::launch_allreduce(c.format, c.scale, c.block, dt, p, k, n, two_shot ? 1 : 0, out,
+                                         two_shot ? packed_out : nullptr, static_cast<hipStream_t>(stream)));
+}
+
 rc_status rc_copy(const void* in, void* out, size_t bytes, void* stream)
 {
     if (bytes == 0) return RC_OK;

@@ -85,4 +85,16 @@ hipError_t launch_reduce(int fmt, int sc, int bl, const StreamPtrs& p, int k, si
     return e ? e->r(p, k, n, out, sum, st) : hipErrorInvalidValue;
 }
 
+// The fused all-reduce emulation exists for the four default codecs.
+hipError_t launch_allreduce(int fmt, int sc, int bl, int dtype, const StreamPtrs& msgs, int k, size_t n, int two_shot,
+                            void* out, void* packed, hipStream_t st)
+{
+    if (bl != 32) return hipErrorInvalidValue;
+    if (fmt == kInt4 && sc == S16) return launch_allreduce_t<kInt4, S16, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
+    if (fmt == kInt3 && sc == S16) return launch_allreduce_t<kInt3, S16, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
+    if (fmt == kFp8 && sc == S32) return launch_allreduce_t<kFp8, S32, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
+    if (fmt == kMx4 && sc == SE8) return launch_allreduce_t<kMx4, SE8, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace rc

@@ -155,9 +155,10 @@ __device__ __forceinline__ void accumulate(const LaneBlock<FMT, SC, BL>& b, floa
     }
 }
 
-// Quantize the lane's 32 values and store its code words and scale(s).
+// Quantize the lane's 32 values into its code words and scale bits (in
+// registers).
 template <int FMT, int SC, int BL>
-__device__ __forceinline__ void encode_store_buf(const float (&v)[32], Rsrc r, uint32_t lane)
+__device__ __forceinline__ LaneBlock<FMT, SC, BL> encode_lane(const float (&v)[32])
 {
     constexpr int H = Halves<BL>::v;
     float a[H];
@@ -165,40 +166,57 @@ __device__ __forceinline__ void encode_store_buf(const float (&v)[32], Rsrc r, u
     EncScale sc[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) sc[h] = enc_scale<FMT, SC>(a[h]);
+    LaneBlock<FMT, SC, BL> b;
+#pragma unroll
+    for (int h = 0; h < H; ++h) b.sbits[h] = sc[h].bits;
     if constexpr (FMT == kInt3) {
         const Int3Words w = int3_encode<H>(v, sc);
-        __builtin_amdgcn_raw_buffer_store_b64((u32x2){w.w0, w.w1}, r, lane * 8u, 0, kNT);
-        __builtin_amdgcn_raw_buffer_store_b32(w.h, r, 512u + lane * 4u, 0, kNT);
+        b.c.w0 = w.w0; b.c.w1 = w.w1; b.c.h = w.h;
     } else if constexpr (FMT == kInt4) {
-        uint32_t D[4];
-        int4_encode<H>(v, sc, D);
-        __builtin_amdgcn_raw_buffer_store_b128((u32x4){D[0], D[1], D[2], D[3]}, r, lane * 16u, 0, kNT);
+        int4_encode<H>(v, sc, b.c.d);
     } else if constexpr (FMT == kFp8 || FMT == kBf8) {
-        uint32_t d[8];
-        fp8_encode<FMT, SC, H>(v, sc, d);
-        __builtin_amdgcn_raw_buffer_store_b128((u32x4){d[0], d[1], d[2], d[3]}, r, lane * 32u, 0, kNT);
-        __builtin_amdgcn_raw_buffer_store_b128((u32x4){d[4], d[5], d[6], d[7]}, r, lane * 32u + 16u, 0, kNT);
+        fp8_encode<FMT, SC, H>(v, sc, b.c.d);
     } else {
-        uint32_t D[4];
-        mx_encode<H>(v, sc, D);
-        __builtin_amdgcn_raw_buffer_store_b128((u32x4){D[0], D[1], D[2], D[3]}, r, lane * 16u, 0, kNT);
+        mx_encode<H>(v, sc, b.c.d);
+    }
+    return b;
+}
+
+// Store the lane's code words and scale(s) into a tile.
+template <int FMT, int SC, int BL>
+__device__ __forceinline__ void store_lane_block(const LaneBlock<FMT, SC, BL>& b, Rsrc r, uint32_t lane)
+{
+    if constexpr (FMT == kInt3) {
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){b.c.w0, b.c.w1}, r, lane * 8u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b32(b.c.h, r, 512u + lane * 4u, 0, kNT);
+    } else if constexpr (FMT == kFp8 || FMT == kBf8) {
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[0], b.c.d[1], b.c.d[2], b.c.d[3]}, r, lane * 32u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[4], b.c.d[5], b.c.d[6], b.c.d[7]}, r, lane * 32u + 16u, 0, kNT);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[0], b.c.d[1], b.c.d[2], b.c.d[3]}, r, lane * 16u, 0, kNT);
     }
     constexpr uint32_t base = Fmt<FMT>::code_bytes;
     constexpr uint32_t SB = ScaleBytes<SC>::v;
     if constexpr (BL == 16) {
-        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b32(sc[0].bits | (sc[1].bits << 16), r, base + lane * 4u, 0, kNT);
-        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b64((u32x2){sc[0].bits, sc[1].bits}, r, base + lane * 8u, 0, kNT);
-        else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(sc[0].bits | (sc[1].bits << 8)), r, base + lane * 2u, 0, kNT);
+        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b32(b.sbits[0] | (b.sbits[1] << 16), r, base + lane * 4u, 0, kNT);
+        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b64((u32x2){b.sbits[0], b.sbits[1]}, r, base + lane * 8u, 0, kNT);
+        else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(b.sbits[0] | (b.sbits[1] << 8)), r, base + lane * 2u, 0, kNT);
     } else if constexpr (BL == 32) {
-        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sc[0].bits, r, base + lane * 2u, 0, kNT);
-        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b32(sc[0].bits, r, base + lane * 4u, 0, kNT);
-        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc[0].bits, r, base + lane, 0, kNT);
+        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b.sbits[0], r, base + lane * 2u, 0, kNT);
+        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b32(b.sbits[0], r, base + lane * 4u, 0, kNT);
+        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b.sbits[0], r, base + lane, 0, kNT);
     } else if ((lane & 1u) == 0u) {                  // 64: the even lane of the pair stores
         const uint32_t idx = lane >> 1;
-        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sc[0].bits, r, base + idx * 2u, 0, kNT);
-        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b32(sc[0].bits, r, base + idx * 4u, 0, kNT);
-        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc[0].bits, r, base + idx, 0, kNT);
+        if constexpr (SB == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b.sbits[0], r, base + idx * 2u, 0, kNT);
+        else if constexpr (SB == 4) __builtin_amdgcn_raw_buffer_store_b32(b.sbits[0], r, base + idx * 4u, 0, kNT);
+        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b.sbits[0], r, base + idx, 0, kNT);
     }
+}
+
+template <int FMT, int SC, int BL>
+__device__ __forceinline__ void encode_store_buf(const float (&v)[32], Rsrc r, uint32_t lane)
+{
+    store_lane_block<FMT, SC, BL>(encode_lane<FMT, SC, BL>(v), r, lane);
 }
 
 __device__ __forceinline__ void wave_lds_sync()
@@ -504,6 +522,110 @@ void unpack_kernel(const uint8_t* __restrict__ in, size_t n, void* __restrict__ 
     }
 }
 
+// ------------------------------------------- fused all-reduce emulation ----
+//
+// A quantized all-reduce of k messages that all sit in this GPU's memory,
+// one per emulated rank, in one pass: for every tile each message is
+// quantized and decoded in registers (what a receiver decodes), the decoded
+// values are added in stream order in binary32, and then either the sum is
+// requantized and decoded once more (two-shot: reduce-scatter and
+// all-gather both carry compressed data) or written as is (one-shot: every
+// rank reads all compressed messages).  Nothing but the inputs, the output
+// and (optionally) the requantized sum touches memory.
+
+// The lane's 32 input elements of one tile, regrouped through LDS like the
+// quantize kernel's input.
+template <int DT>
+__device__ __forceinline__ void load_lane_row(const void* base, size_t tile, uint32_t lane, uint8_t* lds, float (&v)[32])
+{
+    constexpr int ES = (DT == kF32) ? 4 : 2;
+    constexpr int TIB = kTile * ES;
+    constexpr int BB = 32 * ES;
+    constexpr int CPB = BB / 16;
+    constexpr int ROW = BB + 16;
+    const Rsrc src = span_rsrc(base, tile * TIB, TIB);
+    u32x4 c[CPB];
+#pragma unroll
+    for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (64u * i + lane) * 16u, 0, kNT);
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < CPB; ++i) {
+        const uint32_t ch = 64u * i + lane;
+        *reinterpret_cast<u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16) = c[i];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < CPB; ++i) c[i] = *reinterpret_cast<const u32x4*>(lds + lane * ROW + 16 * i);
+    wave_lds_sync();                             // rows read before the next reuse of the buffer
+    widen_chunks<DT, CPB>(c, v);
+}
+
+// The lane's 32 output values of one tile, regrouped through LDS like the
+// unpack kernel's output.
+template <int DT>
+__device__ __forceinline__ void store_lane_row(void* base, size_t tile, uint32_t lane, uint8_t* lds, const float (&d)[32])
+{
+    constexpr int ES = (DT == kF32) ? 4 : 2;
+    constexpr int OB = 32 * ES;
+    constexpr int CPB = OB / 16;
+    constexpr int ROW = OB + 16;
+    uint32_t wd[32];
+    out_words<DT>(d, wd);
+    const Rsrc dst = span_rsrc(base, tile * (size_t)(kTile * ES), kTile * ES);
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < CPB; ++i)
+        *reinterpret_cast<u32x4*>(lds + lane * ROW + 16 * i) = (u32x4){wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]};
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < CPB; ++i) {
+        const uint32_t ch = 64u * i + lane;
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16),
+                                               dst, ch * 16u, 0, kNT);
+    }
+    wave_lds_sync();
+}
+
+// Built for 4 waves per SIMD (up to 128 VGPRs): the message row, the FP32
+// sums and the codes are live together.
+template <int FMT, int SC, int BL, int DT, bool TWO_SHOT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void allreduce_kernel(StreamPtrs msgs, int k, size_t n, void* __restrict__ out, uint8_t* __restrict__ packed_out,
+                      size_t tiles)
+{
+    constexpr int ES = (DT == kF32) ? 4 : 2;
+    constexpr int ROW = 32 * ES + 16;
+    constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    const TileWalk tw = tile_walk();
+    const uint32_t lane = (uint32_t)tw.lane;
+    uint8_t* lds = sm[tw.w];
+    const size_t full = n / kTile;
+    for (size_t tile = tw.first; tile < tiles; tile += tw.stride) {
+        const bool partial = tile >= full;        // wave-uniform: only the last tile
+        float acc[32];
+        for (int j = 0; j < k; ++j) {
+            float v[32];
+            if (!partial) load_lane_row<DT>(msgs.p[j], tile, lane, lds, v);
+            else load_block<DT>(msgs.p[j], tile * kTile + (size_t)lane * 32, n, v);
+            const LaneBlock<FMT, SC, BL> b = encode_lane<FMT, SC, BL>(v);
+            if (j == 0) accumulate<FMT, SC, BL, true>(b, acc);
+            else accumulate<FMT, SC, BL, false>(b, acc);
+        }
+        float d[32];
+        if constexpr (TWO_SHOT) {
+            const LaneBlock<FMT, SC, BL> r = encode_lane<FMT, SC, BL>(acc);
+            if (packed_out) store_lane_block<FMT, SC, BL>(r, span_rsrc(packed_out, tile * TB, TB), lane);
+            accumulate<FMT, SC, BL, true>(r, d);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) d[e] = acc[e];
+        }
+        if (!partial) store_lane_row<DT>(out, tile, lane, lds, d);
+        else store_block_guarded<DT>(out, tile * kTile + (size_t)lane * 32, n, d);
+    }
+}
+
 // ---------------------------------------------------------- launchers ----
 
 // Grid of four-wave workgroups: one tile per wave up to RC_GROUPS_PER_CU
@@ -576,6 +698,23 @@ hipError_t launch_reduce_unrolled_t(const StreamPtrs& p, int k, size_t n, void* 
     case 15: return launch_reduce_k<FMT, SC, BL, 15>(p, k, n, out, sum, st);
     default: return launch_reduce_k<FMT, SC, BL, 16>(p, k, n, out, sum, st);
     }
+}
+
+template <int FMT, int SC, int BL>
+hipError_t launch_allreduce_t(int dt, const StreamPtrs& msgs, int k, size_t n, int two_shot, void* out, void* packed,
+                              hipStream_t st)
+{
+    const size_t tiles = (n + kTile - 1) / kTile;
+    uint8_t* po = static_cast<uint8_t*>(packed);
+#define RC_AR(DT, TS) hipLaunchKernelGGL((allreduce_kernel<FMT, SC, BL, DT, TS>), tile_grid(tiles), dim3(256), 0, st, \
+                                         msgs, k, n, out, po, tiles)
+    if (two_shot) {
+        if (dt == kF32) RC_AR(kF32, true); else if (dt == kF16) RC_AR(kF16, true); else RC_AR(kBF16, true);
+    } else {
+        if (dt == kF32) RC_AR(kF32, false); else if (dt == kF16) RC_AR(kF16, false); else RC_AR(kBF16, false);
+    }
+#undef RC_AR
+    return hipGetLastError();
 }
 
 // Reduce with the stream count a run-time loop (one kernel for every k).

@@ -28,12 +28,18 @@ hipError_t launch_reduce_unrolled_t(const StreamPtrs& p, int k, size_t n, void* 
 template <int FMT, int SC, int BL>
 hipError_t launch_reduce_rt_t(const StreamPtrs& p, int k, size_t n, void* out, float* sum, hipStream_t st);
 
+template <int FMT, int SC, int BL>
+hipError_t launch_allreduce_t(int dtype, const StreamPtrs& msgs, int k, size_t n, int two_shot, void* out,
+                              void* packed, hipStream_t st);
+
 // Codec dispatch (rc_dispatch.cpp): hipErrorInvalidValue for an unsupported
 // (format, scale, block) -- the C ABI checks codecs before calling.
 hipError_t launch_quantize(int fmt, int sc, int bl, int dtype, const void* in, size_t n, void* out, hipStream_t st);
 hipError_t launch_unpack(int fmt, int sc, int bl, const void* in, size_t n, int dtype, void* out, hipStream_t st);
 hipError_t launch_reduce(int fmt, int sc, int bl, const StreamPtrs& p, int k, size_t n, void* out, float* sum,
                          hipStream_t st);
+hipError_t launch_allreduce(int fmt, int sc, int bl, int dtype, const StreamPtrs& msgs, int k, size_t n, int two_shot,
+                            void* out, void* packed, hipStream_t st);
 hipError_t launch_copy(const void* in, void* out, size_t bytes, hipStream_t st);
 
 }  // namespace rc

@@ -160,3 +160,25 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "rcodec_oracle" not in text and "rco_" not in text, f
+
+
+def test_allreduce_emulate_error_paths():
+    l = rca.lib()
+
+    def ar(codec, dt, ptrs, k, n, out, packed=None, two_shot=1):
+        arr = None if ptrs is None else (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+        return l.rc_allreduce_emulate(codec, dt, arr, k, n, two_shot, out, packed, None)
+
+    assert ar(rca.ALL_CODECS["int3_e8m0_b32"], 3, [A], 1, 10, A) == rca.ERR_UNSUPPORTED   # default codecs only
+    assert ar(rca.ALL_CODECS["int3_f16_b16"], 3, [A], 1, 10, A) == rca.ERR_UNSUPPORTED
+    assert ar(rca.INT3, 9, [A], 1, 10, A) == rca.ERR_UNSUPPORTED
+    assert ar(rca.INT3, 3, [A], 0, 10, A) == rca.ERR_RANGE
+    assert ar(rca.INT3, 3, [A] * 17, 17, 10, A) == rca.ERR_RANGE
+    assert ar(rca.INT3, 3, None, 2, 10, A) == rca.ERR_NULL
+    assert ar(rca.INT3, 3, [A, None], 2, 10, A) == rca.ERR_NULL
+    assert ar(rca.INT3, 3, [A, A], 2, 10, None) == rca.ERR_NULL
+    assert ar(rca.INT3, 3, [A, M], 2, 10, A) == rca.ERR_ALIGN
+    assert ar(rca.INT3, 3, [A, A], 2, 10, M) == rca.ERR_ALIGN
+    assert ar(rca.INT3, 3, [A, A], 2, 10, A, M) == rca.ERR_ALIGN
+    assert ar(rca.INT3, 3, [A, A], 2, 0, A) == rca.OK
+    assert ar(rca.INT3, 3, [A, A], 2, (1 << 40) + 1, A) == rca.ERR_RANGE

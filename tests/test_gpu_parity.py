@@ -423,3 +423,23 @@ def test_variant_reduce_bit_exact(name, k):
     assert_same(got[:pb], ref, name)
     assert (got[pb:] == 0xA5).all()
     assert_sums(sums.cpu().numpy(), ref_sum)
+
+
+# ------------------------------------------------ fused all-reduce emulation ----
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("two_shot", [True, False])
+@pytest.mark.parametrize("k", [1, 2, 4, 5])
+def test_allreduce_emulate_bit_exact(fmt, dt, two_shot, k):
+    n = 2 * 2048 + 900
+    say(f"case allreduce fmt={fmt} dt={dt} two_shot={two_shot} k={k}")
+    msgs = [mixed(n, seed=300 * k + 17 * j + len(fmt), dt=dt) for j in range(k)]
+    ref, ref_packed = oracle.allreduce_emulate(oracle.CODECS[fmt], msgs, ORACLE_DT[dt], two_shot=two_shot)
+    out, packed = rca.allreduce_emulate([to_dev(m, dt) for m in msgs], rca.CODECS[fmt], two_shot=two_shot,
+                                        packed_out=two_shot)
+    g = out.cpu()
+    g = g.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else g.numpy()
+    assert_same(g, ref, f"allreduce {fmt} {dt}")
+    if two_shot:
+        assert_same(host_u8(packed), ref_packed, "packed sum")

@@ -147,3 +147,26 @@ def test_status_codes():
     assert lib.rco_quantize_pack(oracle.Codec(1, 2, 32), 1, None, 10, None) == oracle.ERR_UNSUPPORTED
     assert lib.rco_quantize_pack(oracle.Codec(*oracle.INT4), 1, None, 10, None) == oracle.ERR_NULL
     assert lib.rco_quantize_pack(oracle.Codec(*oracle.INT4), 1, None, 0, None) == oracle.OK
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_allreduce_emulation_is_the_composed_pipeline(fmt):
+    """The emulated all-reduce: two-shot = unpack of the requantized sum,
+    one-shot = the FP32 sums rounded to the messages' dtype; with K copies of
+    one INT/MX message (K a power of two) the two-shot result is K times the
+    one-message round trip, exactly."""
+    c = oracle.CODECS[fmt]
+    n = 2048 + 500
+    msgs = [(np.random.default_rng(j).standard_normal(n) * (j + 1)).astype(np.float32) for j in range(3)]
+    out2, packed = oracle.allreduce_emulate(c, msgs, oracle.DT_FP32, two_shot=True)
+    streams = [oracle.quantize_pack(c, m) for m in msgs]
+    red, sums = oracle.dequant_reduce_requant(c, streams, n, want_sum=True)
+    assert np.array_equal(packed, red)
+    assert np.array_equal(out2.view(np.uint32), oracle.unpack_dequant(c, red, n).view(np.uint32))
+    out1, _ = oracle.allreduce_emulate(c, msgs, oracle.DT_FP32, two_shot=False)
+    assert np.array_equal(out1.view(np.uint32), sums.view(np.uint32))
+    if fmt != "fp8":
+        x = msgs[0]
+        one = oracle.unpack_dequant(c, oracle.quantize_pack(c, x), n)
+        four, _ = oracle.allreduce_emulate(c, [x] * 4, oracle.DT_FP32, two_shot=True)
+        assert np.array_equal(four, one * np.float32(4))
