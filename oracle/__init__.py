@@ -85,6 +85,7 @@ def _load():
         "rco_fp8_scale": (ctypes.c_float, [ctypes.c_float]),
         "rco_mx_exponent": (i32, [ctypes.c_float]),
         "rco_e5m2_decode": (ctypes.c_float, [ctypes.c_uint8]),
+        "rco_mxfp4_gemv": (i32, [vp, sz, sz, i32, vp, i32, vp]),
         "rco_e5m2_mag_of_quotient": (i32, [ctypes.c_double, ctypes.c_double]),
         "rco_elem_emax": (i32, [i32]),
         "rco_e8m0_exponent": (i32, [ctypes.c_float, i32]),
@@ -341,3 +342,16 @@ def allreduce_emulate(c, msgs, dtype: int, two_shot: bool = True):
     if dtype == DT_FP16:
         return f32_to_f16_bits(sums).view(np.float16), packed
     return f32_to_bf16_bits(sums), packed
+
+
+def mxfp4_gemv(w_packed: np.ndarray, rows: int, cols: int, x: np.ndarray, x_dtype: int | None = None,
+               y_dtype: int = DT_FP32) -> np.ndarray:
+    """y = W x on an MXFP4-packed row-major matrix (see rco_mxfp4_gemv for
+    the summation order).  x: float32 / float16 / uint16 bf16 bits."""
+    w_packed = np.ascontiguousarray(w_packed, dtype=np.uint8)
+    x = np.ascontiguousarray(x)
+    if w_packed.size < packed_bytes(MXFP4, rows * cols) or x.size < cols:
+        raise ValueError("w_packed or x too small")
+    y = np.empty(rows, dtype=np.float32 if y_dtype == DT_FP32 else np.uint16)
+    _check(_load().rco_mxfp4_gemv(_ptr(w_packed), rows, cols, _dtype_code(x, x_dtype), _ptr(x), y_dtype, _ptr(y)))
+    return y.view(np.float16) if y_dtype == DT_FP16 else y

@@ -648,3 +648,57 @@ void rco_map_e8m0_exponent(const float *amax, int emax, int32_t *y, size_t n)
 { for (size_t i = 0; i < n; ++i) y[i] = rco_e8m0_exponent(amax[i], emax); }
 void rco_map_fp8_scale_f16_bits(const float *amax, int format, uint16_t *y, size_t n)
 { for (size_t i = 0; i < n; ++i) y[i] = rco_fp8_scale_f16_bits(amax[i], format); }
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 GEMV on packed tiles                                          */
+/* ------------------------------------------------------------------ */
+
+/* y = W x for a row-major rows x cols matrix W packed as MXFP4 tiles (row r
+ * = tiles r*T .. r*T+T-1, T = cols/2048), the consumer of the packed layout
+ * ("ML-SpecQD: Multi-Level Speculative Decoding with Quantized Drafts",
+ * abstract: MXFP4 weights direct-cast from BF16).  The pages fix no
+ * summation order; this one is the definition (written out step by step):
+ *   block term  t_b = 2^e_b * (fma chain over the block's 32 elements in
+ *               order, starting from +0: p = fma(code value, x, p));
+ *   lane sums   L_l = t_l, then L_l = RN32(L_l + t_{64j+l}) for j = 1..T-1;
+ *   butterfly   for off = 32, 16, 8, 4, 2, 1: L_l = RN32(L_l + L_{l^off})
+ *               (all lanes at once, from the previous level's values);
+ *   y[r]        = L_0 rounded to y's dtype (RNE).
+ * Binary32 fmaf/ldexpf are single IEEE roundings (subnormal results kept). */
+int rco_mxfp4_gemv(const void *w, size_t rows, size_t cols, int x_dtype, const void *x,
+                   int y_dtype, void *y)
+{
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return RCO_ERR_UNSUPPORTED;
+    if (cols == 0 || cols % RCO_TILE_ELEMS != 0) return RCO_ERR_RANGE;
+    if (rows == 0) return RCO_OK;
+    if (!w || !x || !y) return RCO_ERR_NULL;
+    const rco_codec c = {RCO_FMT_MXFP4, RCO_SCALE_E8M0, 32};
+    const size_t tb = rco_tile_bytes(c), T = cols / RCO_TILE_ELEMS;
+    for (size_t r = 0; r < rows; ++r) {
+        float lane[64];
+        for (int l = 0; l < 64; ++l) {
+            for (size_t j = 0; j < T; ++j) {
+                const uint8_t *tile = (const uint8_t *)w + (r * T + j) * tb;
+                float p = 0.0f;
+                for (int e = 0; e < 32; ++e) {
+                    const int i = 32 * l + e;                       /* element in the tile */
+                    const float code = rco_e2m1_decode((uint8_t)get_bits(tile, 4 * (size_t)i, 4));
+                    const float xv = widen(x_dtype, x, j * RCO_TILE_ELEMS + (size_t)i);
+                    p = fmaf(code, xv, p);
+                }
+                const uint8_t sb = tile[1024 + l];
+                const float t = (sb == 0xFF) ? NAN : ldexpf(p, (int)sb - 127);
+                lane[l] = (j == 0) ? t : lane[l] + t;
+            }
+        }
+        for (int off = 32; off >= 1; off /= 2) {
+            float nxt[64];
+            for (int l = 0; l < 64; ++l) nxt[l] = lane[l] + lane[l ^ off];
+            memcpy(lane, nxt, sizeof lane);
+        }
+        if (y_dtype == RCO_DT_FP32)      ((float *)y)[r] = lane[0];
+        else if (y_dtype == RCO_DT_FP16) ((uint16_t *)y)[r] = rco_f32_to_f16(lane[0]);
+        else                             ((uint16_t *)y)[r] = rco_f32_to_bf16(lane[0]);
+    }
+    return RCO_OK;
+}

@@ -395,3 +395,55 @@ def reduce_codec(c, streams, n: int):
         sums[t * TILE:t * TILE + lim] = acc[:lim]
         out += encode_codec(c, acc)
     return out, sums
+
+
+# ---- MXFP4 GEMV in exact rationals -----------------------------------------
+
+def rn32(q: Fraction) -> Fraction:
+    """Round a rational to the nearest binary32 value, ties to even
+    (subnormals included); returns the rounded value as a Fraction."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = _floor_log2(a)
+    e = max(e, -126)                                 # subnormal quantum 2^-149
+    scale = Fraction(2) ** (23 - e)
+    m = a * scale
+    k = m.numerator // m.denominator
+    rem = m - k
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    if k >= 2 ** 24 and e + 1 > 127:
+        raise OverflowError
+    return sign * Fraction(k) / scale
+
+
+def gemv_mxfp4(w_packed: bytes, rows: int, cols: int, x: np.ndarray):
+    """y = W x in the defined order: per block an fma chain (exact product,
+    one rounding per step) from +0, times 2^e rounded once; per lane the
+    block terms of its tiles in tile order; then the xor butterfly over the
+    64 lanes with offsets 32, 16, 8, 4, 2, 1.  Returns float32 values."""
+    tb = codec_tile_bytes((4, 3, 32))
+    T = cols // TILE
+    xs = [Fraction(float(v)) for v in np.asarray(x, dtype=np.float32)]
+    out = []
+    for r in range(rows):
+        lane = []
+        for l in range(64):
+            acc = None
+            for j in range(T):
+                tile = w_packed[(r * T + j) * tb:(r * T + j + 1) * tb]
+                p = Fraction(0)
+                for e in range(32):
+                    i = 32 * l + e
+                    nb = (tile[i // 2] >> (4 * (i % 2))) & 15
+                    code = -E2M1[nb & 7] if nb & 8 else E2M1[nb & 7]
+                    p = rn32(p + code * xs[j * TILE + i])
+                t = rn32(p * Fraction(2) ** (tile[1024 + l] - 127))
+                acc = t if acc is None else rn32(acc + t)
+            lane.append(acc)
+        for off in (32, 16, 8, 4, 2, 1):
+            lane = [rn32(lane[l] + lane[l ^ off]) for l in range(64)]
+        out.append(np.float32(float(lane[0])))
+    return np.array(out, dtype=np.float32)
