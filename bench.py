@@ -67,6 +67,8 @@ def parse_args():
     ap.add_argument("--table-codecs", default="int3,int4,fp8,mxfp4",
                     help="comma list of codec names (default names or <elem>_<scale>_b<block>), or 'all'")
     ap.add_argument("--table-k", default="2,4,8", help="stream counts of the reduce rows")
+    ap.add_argument("--gemv", action="store_true",
+                    help="MXFP4 GEMV on the 4096x4096 weight recipe (no JSON line)")
     ap.add_argument("--fused", action="store_true",
                     help="fused all-reduce emulation against the separate kernels (no JSON line)")
     return ap.parse_args()
@@ -158,6 +160,8 @@ def main():
         return table(args)
     if args.fused:
         return fused_table(args)
+    if args.gemv:
+        return gemv_table(args)
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU only: this codec build has no multi-GPU path "
                          "(run with --gpus 1)\n")
@@ -438,6 +442,66 @@ def fused_table(args):
                 del streams, out, packed
             del msgs
             torch.cuda.empty_cache()
+    return 0
+
+
+def gemv_table(args):
+    """y = W x with W the 4096 x 4096 bf16 weight recipe packed as MXFP4
+    (8.9 MB): one weight matrix (resident in the 256 MiB Infinity Cache after
+    the first call) and a rotation over 64 copies (570 MB, so every call reads
+    HBM).  HBM bytes per call = packed weights + x + y.  torch's bf16 matrix
+    vector product of the unquantized weights is printed for context."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import reduction_codec_amd as rca
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = cols = 4096
+    wb = torch.from_numpy(datagen.bf16_weight_4096x4096().view(np.int16)).view(torch.bfloat16).to(dev)
+    p = rca.quantize_pack(wb, rca.MXFP4)
+    x = torch.from_numpy(np.random.default_rng(5).standard_normal(cols).astype(np.float32)).to(dev).to(torch.bfloat16)
+    copies = [p] + [p.clone() for _ in range(63)]
+    ys = [torch.empty(rows, dtype=torch.float32, device=dev) for _ in range(64)]
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    pb = p.numel()
+    hbm = pb + 2 * cols + 4 * rows
+    print("| case | us | GB/s (packed weights + x + y) | % of peak | weights/s |")
+    print("|---|---:|---:|---:|---:|")
+    for name, fn in (("MXFP4 GEMV, one weight matrix (cache-resident)",
+                      lambda i: rca.mxfp4_gemv(p, rows, cols, x, out=ys[0])),
+                     ("MXFP4 GEMV, 64 rotating weight matrices (HBM)",
+                      lambda i: rca.mxfp4_gemv(copies[i % 64], rows, cols, x, out=ys[i % 64]))):
+        t = timed(fn, 64)
+        g = hbm / (t * 1e-3) / 1e9
+        print(f"| {name} | {t * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | {rows * cols / (t * 1e-3) / 1e12:.2f} T |",
+              flush=True)
+    wm = wb.view(rows, cols)
+    wcopies = [wm] + [wm.clone() for _ in range(15)]
+    xv = x.view(cols, 1)
+    t = timed(lambda i: torch.mm(wcopies[i % 16], xv), 32)
+    g = (2 * rows * cols + 2 * cols + 2 * rows) / (t * 1e-3) / 1e9
+    print(f"| torch bf16 mm (unquantized weights, 16 rotating copies), context | {t * 1e3:.2f} | {g:.0f} | "
+          f"{100 * g / HBM_PEAK_GBS:.1f} | {rows * cols / (t * 1e-3) / 1e12:.2f} T |", flush=True)
     return 0
 
 

@@ -154,6 +154,21 @@ rc_status rc_dequant_reduce_requant(rc_codec c, const void *const *ins, int k, s
 rc_status rc_allreduce_emulate(rc_codec c, rc_dtype dt, const void *const *msgs, int k, size_t n,
                                int two_shot, void *out, void *packed_out, void *stream);
 
+/* y = W x for a row-major rows x cols matrix W held as an MXFP4 packed stream
+ * (rc_quantize_pack of its rows * cols elements with {MXFP4, E8M0, 32}), the
+ * consumer of the packed layout ("ML-SpecQD: Multi-Level Speculative Decoding
+ * with Quantized Drafts", abstract: MXFP4 weights direct-cast from BF16).
+ * cols must be a positive multiple of 2048 (row r = tiles r*cols/2048 ...),
+ * else RC_ERR_RANGE.  x: cols elements of x_t; y: rows elements of y_t.
+ * Summation order (bit-exact with the oracle): lane l of a row owns block
+ * 64j + l of the row's tile j; a block term is an fp32 fma chain over the
+ * block's 32 elements in order from +0, times 2^e (one rounding); the lane
+ * adds its block terms in tile order; the 64 lane sums are added by an xor
+ * butterfly (offsets 32, 16, 8, 4, 2, 1); y is rounded to y_t (RNE).
+ * Pointers are device pointers, 16-byte aligned. */
+rc_status rc_mxfp4_gemv(const void *w, size_t rows, size_t cols, rc_dtype x_t, const void *x,
+                        rc_dtype y_t, void *y, void *stream);
+
 /* Plain device-to-device copy of `bytes` bytes (multiple of 16) with the same
  * 16-byte vector loads/stores as the codec kernels: the bandwidth baseline
  * the codec kernels are measured against. */

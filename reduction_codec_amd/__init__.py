@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     l.rc_dequant_reduce_requant.restype = i32
     l.rc_dequant_reduce_requant.argtypes = [Codec, ctypes.POINTER(vp), i32, sz, vp, vp, vp]
     l.rc_copy.restype, l.rc_copy.argtypes = i32, [vp, vp, sz, vp]
+    l.rc_mxfp4_gemv.restype = i32
+    l.rc_mxfp4_gemv.argtypes = [vp, sz, sz, i32, vp, i32, vp, vp]
     l.rc_allreduce_emulate.restype = i32
     l.rc_allreduce_emulate.argtypes = [Codec, i32, ctypes.POINTER(vp), i32, sz, i32, vp, vp, vp]
     l.rc_status_str.restype, l.rc_status_str.argtypes = ctypes.c_char_p, [i32]
@@ -238,6 +240,28 @@ def allreduce_emulate(msgs, codec, two_shot: bool = True, out: torch.Tensor | No
                                    packed.data_ptr() if packed is not None else None, _stream(stream)),
         "rc_allreduce_emulate")
     return out, packed
+
+
+def mxfp4_gemv(w_packed: torch.Tensor, rows: int, cols: int, x: torch.Tensor, out_dtype=torch.float32,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = W x with W (rows x cols, row-major) packed by quantize_pack with the
+    MXFP4 codec; cols a multiple of 2048.  See rc_mxfp4_gemv."""
+    _check_dev(w_packed, "w_packed")
+    _check_dev(x, "x")
+    if w_packed.dtype != torch.uint8 or w_packed.numel() < packed_bytes(MXFP4, rows * cols):
+        raise ValueError("w_packed must hold packed_bytes(MXFP4, rows * cols) bytes")
+    if x.dtype not in _DTYPES or x.numel() < cols:
+        raise ValueError("x must hold cols fp32 / fp16 / bf16 values")
+    if out_dtype not in _DTYPES:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    if out is None:
+        out = torch.empty(rows, dtype=out_dtype, device=x.device)
+    _check_dev(out, "out")
+    if out.dtype != out_dtype or out.numel() < rows:
+        raise ValueError("out must hold rows values of out_dtype")
+    _ok(lib().rc_mxfp4_gemv(w_packed.data_ptr(), rows, cols, _DTYPES[x.dtype], x.data_ptr(), _DTYPES[out_dtype],
+                            out.data_ptr(), _stream(stream)), "rc_mxfp4_gemv")
+    return out
 
 
 def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> torch.Tensor:

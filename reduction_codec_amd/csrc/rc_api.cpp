@@ -116,6 +116,18 @@ rc_status rc_allreduce_emulate(rc_codec c, rc_dtype dt, const void* const* msgs,
                                          two_shot ? packed_out : nullptr, static_cast<hipStream_t>(stream)));
 }
 
+rc_status rc_mxfp4_gemv(const void* w, size_t rows, size_t cols, rc_dtype x_t, const void* x, rc_dtype y_t,
+                         void* y, void* stream)
+{
+    if (!dtype_ok(x_t) || !dtype_ok(y_t)) return RC_ERR_UNSUPPORTED;
+    if (cols == 0 || cols % RC_TILE_ELEMS != 0 || cols > kMaxElems) return RC_ERR_RANGE;
+    if (rows == 0) return RC_OK;
+    if (rows > kMaxElems / cols) return RC_ERR_RANGE;
+    if (!w || !x || !y) return RC_ERR_NULL;
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return RC_ERR_ALIGN;
+    return from_hip(rc::launch_mxfp4_gemv(w, rows, cols, x_t, x, y_t, y, static_cast<hipStream_t>(stream)));
+}
+
 rc_status rc_copy(const void* in, void* out, size_t bytes, void* stream)
 {
     if (bytes == 0) return RC_OK;

@@ -626,6 +626,122 @@ void allreduce_kernel(StreamPtrs msgs, int k, size_t n, void* __restrict__ out, 
     }
 }
 
+// ------------------------------------------------------------ MXFP4 GEMV ----
+//
+// y = W x on an MXFP4-packed row-major matrix (row r = tiles r*T .. r*T+T-1).
+// The summation order is the definition: lane l of a row owns block 64j + l
+// of tile j; a block term is an fma chain over its 32 elements in order from
+// +0, times 2^e (one rounding, v_ldexp); the lane adds its block terms in
+// tile order; then an xor butterfly over the 64 lanes (offsets 32..1); lane 0
+// writes y[r].  One wave per row, R rows per wave iteration; with T <= 2 the
+// lane's x values live in registers across rows.
+
+// The lane's 32 x values of tile j (elements j*2048 + 32 lane .. + 31).
+template <int XT>
+__device__ __forceinline__ void load_x32(Rsrc xr, int j, uint32_t lane, float (&xv)[32])
+{
+    constexpr uint32_t ES = (XT == kF32) ? 4 : 2;
+    const uint32_t off = ((uint32_t)j * kTile + lane * 32u) * ES;
+    if constexpr (XT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0);
+            xv[4 * i] = __uint_as_float(u.x); xv[4 * i + 1] = __uint_as_float(u.y);
+            xv[4 * i + 2] = __uint_as_float(u.z); xv[4 * i + 3] = __uint_as_float(u.w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) widen8<XT>(__builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0), xv + 8 * i);
+    }
+}
+
+// Block term 2^e * (fma chain over the lane's 32 elements of one tile).
+__device__ __forceinline__ float gemv_block_term(Rsrc wt, uint32_t lane, const float (&xv)[32])
+{
+    const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(wt, lane * 16u, 0, kNT);
+    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(wt, 1024u + lane, 0, kNT);
+    const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+    float p = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f2 v = fp4_dec(d[w], 1.0f, b);            // elements 8w+2b, 8w+2b+1
+            p = __builtin_fmaf(v.x, xv[8 * w + 2 * b], p);
+            p = __builtin_fmaf(v.y, xv[8 * w + 2 * b + 1], p);
+        }
+    }
+    return (sb == 255u) ? __builtin_nanf("") : __builtin_ldexpf(p, (int)sb - 127);
+}
+
+__device__ __forceinline__ float butterfly_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int YT>
+__device__ __forceinline__ void store_y(void* y, size_t r, float v)
+{
+    if constexpr (YT == kF32) static_cast<float*>(y)[r] = v;
+    else if constexpr (YT == kBF16) static_cast<uint16_t*>(y)[r] = __bfloat16_as_ushort(__float2bfloat16(v));
+    else static_cast<uint16_t*>(y)[r] = (uint16_t)f16_bits(v);
+}
+
+// TC = T when T <= 2 (x in registers), 0 for any T (x reloaded per tile).
+template <int XT, int YT, int TC>
+__global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restrict__ w, size_t rows, int T,
+                                                         const void* __restrict__ x, void* __restrict__ y)
+{
+    constexpr int TB = TileGeom<kMx4, kSE8, 32>::bytes;
+    constexpr uint32_t ES = (XT == kF32) ? 4 : 2;
+    const TileWalk tw = tile_walk();
+    const uint32_t lane = (uint32_t)tw.lane;
+    const Rsrc xr = span_rsrc(x, 0, (uint32_t)T * kTile * ES);
+    if constexpr (TC > 0) {
+        float xv[TC][32];
+#pragma unroll
+        for (int j = 0; j < TC; ++j) load_x32<XT>(xr, j, lane, xv[j]);
+        size_t r = tw.first;
+        for (; r + tw.stride < rows; r += 2 * tw.stride) {        // two rows at a time
+            float L0 = 0.0f, L1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < TC; ++j) {
+                const float t0 = gemv_block_term(span_rsrc(w, (r * TC + j) * TB, TB), lane, xv[j]);
+                const float t1 = gemv_block_term(span_rsrc(w, ((r + tw.stride) * TC + j) * TB, TB), lane, xv[j]);
+                L0 = (j == 0) ? t0 : L0 + t0;
+                L1 = (j == 0) ? t1 : L1 + t1;
+            }
+            L0 = butterfly_sum(L0);
+            L1 = butterfly_sum(L1);
+            if (lane == 0) { store_y<YT>(y, r, L0); store_y<YT>(y, r + tw.stride, L1); }
+        }
+        if (r < rows) {
+            float L = 0.0f;
+#pragma unroll
+            for (int j = 0; j < TC; ++j) {
+                const float t = gemv_block_term(span_rsrc(w, (r * TC + j) * TB, TB), lane, xv[j]);
+                L = (j == 0) ? t : L + t;
+            }
+            L = butterfly_sum(L);
+            if (lane == 0) store_y<YT>(y, r, L);
+        }
+    } else {
+        for (size_t r = tw.first; r < rows; r += tw.stride) {
+            float L = 0.0f;
+            for (int j = 0; j < T; ++j) {
+                float xv[32];
+                load_x32<XT>(xr, j, lane, xv);
+                const float t = gemv_block_term(span_rsrc(w, (r * (size_t)T + j) * TB, TB), lane, xv);
+                L = (j == 0) ? t : L + t;
+            }
+            L = butterfly_sum(L);
+            if (lane == 0) store_y<YT>(y, r, L);
+        }
+    }
+}
+
 // ---------------------------------------------------------- launchers ----
 
 // Grid of four-wave workgroups: one tile per wave up to RC_GROUPS_PER_CU
@@ -715,6 +831,32 @@ hipError_t launch_allreduce_t(int dt, const StreamPtrs& msgs, int k, size_t n, i
     }
 #undef RC_AR
     return hipGetLastError();
+}
+
+template <int XT, int YT>
+static hipError_t launch_gemv_xy(const void* w, size_t rows, int T, const void* x, void* y, hipStream_t st)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // one row per wave, at most 16 four-wave workgroups per CU (rows loop beyond)
+    size_t groups = (rows + kWavesPerGroup - 1) / kWavesPerGroup;
+    const size_t cap = (size_t)16 * (size_t)(cus > 0 ? cus : 256);
+    if (groups > cap) groups = cap;
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    if (T == 1) hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 1>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
+    else if (T == 2) hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 2>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
+    else hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 0>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
+    return hipGetLastError();
+}
+
+inline hipError_t launch_gemv_impl(const void* w, size_t rows, size_t cols, int xt, const void* x, int yt, void* y,
+                                   hipStream_t st)
+{
+    const int T = (int)(cols / kTile);
+#define RC_G(XT) (yt == kF32 ? launch_gemv_xy<XT, kF32>(w, rows, T, x, y, st) : \
+                  yt == kF16 ? launch_gemv_xy<XT, kF16>(w, rows, T, x, y, st) : launch_gemv_xy<XT, kBF16>(w, rows, T, x, y, st))
+    return xt == kF32 ? RC_G(kF32) : (xt == kF16 ? RC_G(kF16) : RC_G(kBF16));
+#undef RC_G
 }
 
 // Reduce with the stream count a run-time loop (one kernel for every k).

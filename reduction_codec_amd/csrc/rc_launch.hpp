@@ -41,5 +41,8 @@ hipError_t launch_reduce(int fmt, int sc, int bl, const StreamPtrs& p, int k, si
 hipError_t launch_allreduce(int fmt, int sc, int bl, int dtype, const StreamPtrs& msgs, int k, size_t n, int two_shot,
                             void* out, void* packed, hipStream_t st);
 hipError_t launch_copy(const void* in, void* out, size_t bytes, hipStream_t st);
+// y = W x on an MXFP4-packed row-major matrix, cols a multiple of 2048.
+hipError_t launch_mxfp4_gemv(const void* w, size_t rows, size_t cols, int x_dtype, const void* x, int y_dtype,
+                             void* y, hipStream_t st);
 
 }  // namespace rc

@@ -182,3 +182,19 @@ def test_allreduce_emulate_error_paths():
     assert ar(rca.INT3, 3, [A, A], 2, 10, A, M) == rca.ERR_ALIGN
     assert ar(rca.INT3, 3, [A, A], 2, 0, A) == rca.OK
     assert ar(rca.INT3, 3, [A, A], 2, (1 << 40) + 1, A) == rca.ERR_RANGE
+
+
+def test_mxfp4_gemv_error_paths():
+    l = rca.lib()
+    g = lambda w, rows, cols, xt, x, yt, y: l.rc_mxfp4_gemv(w, rows, cols, xt, x, yt, y, None)
+    assert g(A, 4, 4096, 7, A, 1, A) == rca.ERR_UNSUPPORTED
+    assert g(A, 4, 4096, 3, A, 0, A) == rca.ERR_UNSUPPORTED
+    assert g(A, 4, 1000, 3, A, 1, A) == rca.ERR_RANGE
+    assert g(A, 4, 0, 3, A, 1, A) == rca.ERR_RANGE
+    assert g(A, 0, 4096, 3, A, 1, A) == rca.OK
+    assert g(None, 4, 4096, 3, A, 1, A) == rca.ERR_NULL
+    assert g(A, 4, 4096, 3, None, 1, A) == rca.ERR_NULL
+    assert g(A, 4, 4096, 3, A, 1, None) == rca.ERR_NULL
+    assert g(M, 4, 4096, 3, A, 1, A) == rca.ERR_ALIGN
+    assert g(A, 4, 4096, 3, M, 1, A) == rca.ERR_ALIGN
+    assert g(A, 1 << 40, 4096, 3, A, 1, A) == rca.ERR_RANGE

@@ -443,3 +443,36 @@ def test_allreduce_emulate_bit_exact(fmt, dt, two_shot, k):
     assert_same(g, ref, f"allreduce {fmt} {dt}")
     if two_shot:
         assert_same(host_u8(packed), ref_packed, "packed sum")
+
+
+# ------------------------------------------------------------ MXFP4 GEMV ----
+
+@pytest.mark.parametrize("rows,cols", [(1, 2048), (7, 2048), (9, 4096), (33, 6144), (5, 8192)])
+@pytest.mark.parametrize("xt", DTYPES)
+def test_mxfp4_gemv_bit_exact(rows, cols, xt):
+    say(f"case gemv rows={rows} cols={cols} x={xt}")
+    r = np.random.default_rng(rows * 131 + cols)
+    w = mixed(rows * cols, seed=rows + cols, dt="fp32")
+    p = oracle.quantize_pack(oracle.MXFP4, w, dtype=oracle.DT_FP32)
+    x = datagen.narrow((r.standard_normal(cols) * np.exp(r.uniform(-3, 3, cols))).astype(np.float32), xt)
+    for yt in DTYPES:
+        ref = oracle.mxfp4_gemv(p, rows, cols, x, x_dtype=ORACLE_DT[xt], y_dtype=ORACLE_DT[yt])
+        got = rca.mxfp4_gemv(torch.from_numpy(p).to(DEV), rows, cols, to_dev(x, xt), out_dtype=TORCH_DT[yt]).cpu()
+        g = got.view(torch.int16).numpy().view(np.uint16) if yt == "bf16" else got.numpy()
+        assert_same(g, ref, f"gemv y={yt}")
+
+
+def test_mxfp4_gemv_weight_4096x4096_sampled_rows():
+    """The 4096 x 4096 bf16 weight recipe, all rows on the GPU; every 37th row
+    and the last against the oracle."""
+    rows = cols = 4096
+    wbits = datagen.bf16_weight_4096x4096()
+    p = rca.quantize_pack(to_dev(wbits, "bf16"), rca.MXFP4)
+    x = datagen.narrow(np.random.default_rng(5).standard_normal(cols).astype(np.float32), "bf16")
+    y = rca.mxfp4_gemv(p, rows, cols, to_dev(x, "bf16")).cpu().numpy()
+    ph = host_u8(p)
+    pick = list(range(0, rows, 37)) + [rows - 1]
+    tb = oracle.tile_bytes(oracle.MXFP4)
+    sub = np.concatenate([ph[2 * r * tb:(2 * r + 2) * tb] for r in pick])
+    ref = oracle.mxfp4_gemv(sub, len(pick), cols, x, x_dtype=oracle.DT_BF16)
+    assert_same(y[pick], ref, "gemv sampled rows")
