@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "codec GB/s (uncompressed bytes) and % of HBM peak, 64 MB INT3 quant+reduce"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_int3_64MiB.json")
-KERNEL_SOURCES = ["reduction_codec_amd/csrc/rc_device.hpp", "reduction_codec_amd/csrc/rc_kernels.hip"]
+KERNEL_SOURCES = ["reduction_codec_amd/csrc/rc_device.hpp", "reduction_codec_amd/csrc/rc_kernels.hpp",
+                  "reduction_codec_amd/csrc/rc_inst_default.hip"]
 COPY_BYTES = 256 << 20
 
 
