@@ -25,6 +25,11 @@
  *         (element pairs dealt alternately to the group's two 32-bit words).
  *   FP8_E4M3 (2048 B): E4M3 codes (OCP "FN": no infinities, NaN = S.1111.111).
  *   FP8_E5M2 (2048 B): E5M2 codes (bias 15, IEEE infinities and NaNs).
+ *         FP8 byte order: two 1024 B planes; the codes of elements 32g..32g+15
+ *         (the first half of the 32-element group g, whatever the block size)
+ *         at bytes 16g..16g+15, those of 32g+16..32g+31 at 1024+16g.., so the
+ *         codes of 32 consecutive elements are two wave-contiguous 16 B
+ *         accesses.
  *   MXFP4 (1024 B): E2M1 codes (element i in nibble i).
  * Scales: fp16 (2 B) or fp32 (4 B) little-endian, or E8M0 bytes
  * (2^(byte-127), 0xFF = NaN).  The default tiles: INT4 1152 B, INT3 896 B,

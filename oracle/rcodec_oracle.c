@@ -419,6 +419,17 @@ static int int_mag_exact(double y, int qmax)
     return m > qmax ? qmax : m;
 }
 
+/* Byte offset of element i's FP8 code in the tile's code region.  The pages
+ * leave the byte order open; it is fixed as two 1024-byte planes: the first
+ * 16 codes of each 32-element group g (tile elements 32g .. 32g+15, whatever
+ * the block size) at bytes 16g .., the last 16 at 1024 + 16g .., each in
+ * element order. */
+static size_t fp8_code_pos(size_t i)
+{
+    const size_t g = i / 32, e = i % 32;
+    return e < 16 ? 16 * g + e : 1024 + 16 * g + (e - 16);
+}
+
 static void put_code(rco_codec c, uint8_t *dst, size_t i, unsigned sign, unsigned mag)
 {
     switch (c.format) {
@@ -430,7 +441,7 @@ static void put_code(rco_codec c, uint8_t *dst, size_t i, unsigned sign, unsigne
         put_bits(dst + 512, i, sign, 1);
         break;
     default:
-        dst[i] = (uint8_t)((sign << 7) | mag);
+        dst[fp8_code_pos(i)] = (uint8_t)((sign << 7) | mag);
     }
 }
 
@@ -522,8 +533,8 @@ static float decode_elem(rco_codec c, const uint8_t *src, int i)
         val = sign ? -(double)mag : (double)mag;
         break;
     }
-    case RCO_FMT_FP8_E4M3: val = rco_e4m3_decode(src[i]); break;
-    case RCO_FMT_FP8_E5M2: val = rco_e5m2_decode(src[i]); break;
+    case RCO_FMT_FP8_E4M3: val = rco_e4m3_decode(src[fp8_code_pos((size_t)i)]); break;
+    case RCO_FMT_FP8_E5M2: val = rco_e5m2_decode(src[fp8_code_pos((size_t)i)]); break;
     default: val = rco_e2m1_decode((uint8_t)get_bits(src, 4 * (size_t)i, 4));
     }
     if (c.scale == RCO_SCALE_FP32) return (float)val * get_f32(sp);       /* RN32 */

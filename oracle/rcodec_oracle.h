@@ -28,7 +28,9 @@
  * Codecs are (element format, scale type, block size): INT4 and INT3 with
  * FP16 or E8M0 scales; E4M3 and E5M2 with FP32, FP16 or E8M0 scales; E2M1
  * (MXFP4) with E8M0 scales; blocks of 16, 32 or 64 elements.  The tile is
- * always 2048 elements: the code region, then 2048/block scales.
+ * always 2048 elements: the code region, then 2048/block scales.  FP8
+ * codes fill the code region as two 1024-byte planes (the first and the
+ * last 16 codes of every 32-element group).
  * Every step the pages leave open is fixed once here and listed as a
  * "reading" in the design notes of the repository.
  *

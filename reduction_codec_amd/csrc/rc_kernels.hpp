@@ -6,7 +6,8 @@
 // One wave64 per 2048-element tile, lane l = elements 32l..32l+31;
 // 256-thread workgroups (four waves).  Packed tiles are read and written with
 // per-lane buffer accesses that are contiguous across the wave (code words at
-// lane * bytes per 32 elements, scales at lane * scale bytes per lane); the
+// lane * bytes per 32 elements, FP8 codes as two 16-byte planes, scales at
+// lane * scale bytes per lane); the
 // 64- or 128-byte element rows of quantize input and unpack output are
 // regrouped through LDS so that HBM sees wave-coalesced 16-byte chunks.
 #pragma once
@@ -47,6 +48,9 @@ namespace rc {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Per-lane code words of 32 elements of one stream (scales load separately).
+// FP8 codes sit in two 1024-byte planes (the first and the last 16 codes of
+// every 32-element group), so each of a lane's two 16-byte accesses is
+// contiguous across the wave.
 template <int FMT> struct LaneCodes;
 template <> struct LaneCodes<kInt3> { uint32_t w0, w1, h; };
 template <> struct LaneCodes<kInt4> { uint32_t d[4]; };
@@ -82,8 +86,8 @@ __device__ __forceinline__ LaneCodes<FMT> load_codes_buf(Rsrc r, uint32_t lane)
         c.w1 = q.y;
         c.h = __builtin_amdgcn_raw_buffer_load_b32(r, 512u + lane * 4u, 0, kNT);
     } else if constexpr (FMT == kFp8 || FMT == kBf8) {
-        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 32u, 0, kNT);
-        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 32u + 16u, 0, kNT);
+        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, kNT);
+        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(r, 1024u + lane * 16u, 0, kNT);
         c.d[0] = d0.x; c.d[1] = d0.y; c.d[2] = d0.z; c.d[3] = d0.w;
         c.d[4] = d1.x; c.d[5] = d1.y; c.d[6] = d1.z; c.d[7] = d1.w;
     } else {
@@ -190,8 +194,8 @@ __device__ __forceinline__ void store_lane_block(const LaneBlock<FMT, SC, BL>& b
         __builtin_amdgcn_raw_buffer_store_b64((u32x2){b.c.w0, b.c.w1}, r, lane * 8u, 0, kNT);
         __builtin_amdgcn_raw_buffer_store_b32(b.c.h, r, 512u + lane * 4u, 0, kNT);
     } else if constexpr (FMT == kFp8 || FMT == kBf8) {
-        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[0], b.c.d[1], b.c.d[2], b.c.d[3]}, r, lane * 32u, 0, kNT);
-        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[4], b.c.d[5], b.c.d[6], b.c.d[7]}, r, lane * 32u + 16u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[0], b.c.d[1], b.c.d[2], b.c.d[3]}, r, lane * 16u, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[4], b.c.d[5], b.c.d[6], b.c.d[7]}, r, 1024u + lane * 16u, 0, kNT);
     } else {
         __builtin_amdgcn_raw_buffer_store_b128((u32x4){b.c.d[0], b.c.d[1], b.c.d[2], b.c.d[3]}, r, lane * 16u, 0, kNT);
     }

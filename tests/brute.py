@@ -75,6 +75,22 @@ def _words_to_bytes(words) -> bytes:
     return b"".join(int(w & 0xFFFFFFFF).to_bytes(4, "little") for w in words)
 
 
+def fp8_planes(codes) -> bytes:
+    """2048 FP8 codes in element order -> the code region: a plane of the
+    first 16 codes of every 32-element group, then a plane of the last 16."""
+    codes = bytes(codes)
+    assert len(codes) == TILE
+    lo = b"".join(codes[32 * g:32 * g + 16] for g in range(TILE // 32))
+    hi = b"".join(codes[32 * g + 16:32 * g + 32] for g in range(TILE // 32))
+    return lo + hi
+
+
+def fp8_byte(tile: bytes, i: int) -> int:
+    """The FP8 code byte of tile element i."""
+    g, e = divmod(i, 32)
+    return tile[16 * g + e] if e < 16 else tile[1024 + 16 * g + (e - 16)]
+
+
 def encode_tile(fmt: str, v: np.ndarray) -> bytes:
     """v: 2048 float32 values (tail already zero)."""
     v = np.asarray(v, dtype=np.float32)
@@ -131,6 +147,8 @@ def encode_tile(fmt: str, v: np.ndarray) -> bytes:
             raise ValueError(fmt)
     if fmt == "int3":
         return _words_to_bytes(int3_q2w) + _words_to_bytes(int3_q1w) + bytes(scales)
+    if fmt == "fp8":
+        return fp8_planes(codes) + bytes(scales)
     return bytes(codes) + bytes(scales)
 
 
@@ -174,7 +192,7 @@ def decode_tile(fmt: str, tile: bytes) -> np.ndarray:
         elif fmt == "fp8":
             s = np.frombuffer(tile[2048 + 4 * b: 2052 + 4 * b], dtype=np.float32)[0]
             for e in range(32):
-                c = tile[32 * b + e]
+                c = fp8_byte(tile, 32 * b + e)
                 dec = np.float32(float(E4M3[c & 127])) if (c & 127) != 127 else np.float32(np.nan)
                 val = dec * s                      # one binary32 product (IEEE)
                 out[32 * b + e] = -val if c & 128 else val
@@ -325,7 +343,7 @@ def encode_codec(c, x_f32: np.ndarray) -> bytes:
                            ((N[2] >> 1) & 0x44444444) | (N[3] & 0x88888888))
             body = _words_to_bytes(q2w) + _words_to_bytes(q1w)
         else:
-            body = bytes(codes)
+            body = fp8_planes(codes)
         out += body + bytes(scales)
     return out
 
@@ -352,7 +370,7 @@ def decode_codec(c, tile: bytes) -> np.ndarray:
             nib = (((W >> (2 * (k & 1))) & 0x33333333) | ((hw << (3 - k)) & 0x88888888)) >> (4 * j) & 15
             val, neg = Fraction(nib & 7), bool(nib & 8)
         else:
-            code = tile[i]
+            code = fp8_byte(tile, i)
             table = E4M3 if fmt == 3 else E5M2
             if (fmt == 3 and (code & 127) == 127) or (fmt == 5 and (code & 127) >= 124):
                 spec = np.float32(np.nan)

@@ -228,7 +228,9 @@ def test_reduce_ignores_tail_codes(fmt):
         junk[tb + 16:tb + 512] = rng.integers(0, 256, 496, dtype=np.uint8)
         junk[tb + 520:tb + 768] = rng.integers(0, 256, 248, dtype=np.uint8)
     elif fmt == "fp8":
-        junk[tb + 64:tb + 2048] = rng.integers(0, 127, 1984, dtype=np.uint8)
+        # groups 2.. of both code planes (elements 64.., all past n)
+        junk[tb + 32:tb + 1024] = rng.integers(0, 127, 992, dtype=np.uint8)
+        junk[tb + 1056:tb + 2048] = rng.integers(0, 127, 992, dtype=np.uint8)
     else:
         junk[tb + 32:tb + 1024] = rng.integers(0, 256, 992, dtype=np.uint8)
     ref, _ = oracle.dequant_reduce_requant(oracle.CODECS[fmt], [junk, streams[1]], n)

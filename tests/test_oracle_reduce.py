@@ -125,7 +125,9 @@ def test_tail_codes_are_ignored(fmt):
         junk[0][tb + 16:tb + 512] = RNG.integers(0, 256, 496, dtype=np.uint8)
         junk[0][tb + 512 + 8:tb + 768] = RNG.integers(0, 256, 248, dtype=np.uint8)
     elif fmt == "fp8":
-        junk[0][tb + 64:tb + 2048] = RNG.integers(0, 127, 1984, dtype=np.uint8)
+        # groups 2.. of both code planes (elements 64.., all past n)
+        junk[0][tb + 32:tb + 1024] = RNG.integers(0, 127, 992, dtype=np.uint8)
+        junk[0][tb + 1056:tb + 2048] = RNG.integers(0, 127, 992, dtype=np.uint8)
     else:
         junk[0][tb + 32:tb + 1024] = RNG.integers(0, 256, 992, dtype=np.uint8)
     a, _ = oracle.dequant_reduce_requant(codec(fmt), s, n)
