@@ -40,6 +40,14 @@ constexpr int kWavesPerGroup = 4;          // 256-thread workgroups, one tile pe
 // The byte / word selectors of these instructions must be literals; the
 // switches fold away once the callers' loops are unrolled.
 
+// An unspecified 32-bit value: the starting word of a code word whose bytes
+// (or 16-bit halves) are all overwritten by the conversions that follow, so
+// no register has to be cleared first.
+__device__ __forceinline__ uint32_t any_word()
+{
+    return __builtin_nondeterministic_value(0u);
+}
+
 // Two binary32 -> two E2M1 codes (RNE, saturating at 6, sign kept) of
 // a / 2^k and b / 2^k, 2^k = the power-of-two part of `scale`; a goes to the
 // low nibble of byte `sel` of `old`, b to its high nibble.
@@ -395,7 +403,7 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
     uint32_t N[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        uint32_t w = 0u;
+        uint32_t w = any_word();                  // all four bytes are written
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float r = r2[H == 2 ? b / 2 : 0];
@@ -465,8 +473,8 @@ __device__ __forceinline__ void int4_encode(const float (&v)[32], const EncScale
     for (int d = 0; d < 4; ++d) {
         const float r = r9[H == 2 ? d / 2 : 0];
         const float* y = v + 8 * d;
-        xe[d] = fp8_pair(y[4] * r, y[6] * r, fp8_pair(y[0] * r, y[2] * r, 0u, false), true);
-        xo[d] = fp8_pair(y[5] * r, y[7] * r, fp8_pair(y[1] * r, y[3] * r, 0u, false), true);
+        xe[d] = fp8_pair(y[4] * r, y[6] * r, fp8_pair(y[0] * r, y[2] * r, any_word(), false), true);
+        xo[d] = fp8_pair(y[5] * r, y[7] * r, fp8_pair(y[1] * r, y[3] * r, any_word(), false), true);
     }
     bool clamp = sc[0].clamp;
     if constexpr (H == 2) clamp = clamp || sc[1].clamp;
@@ -537,7 +545,7 @@ __device__ __forceinline__ f2 f8_dec(uint32_t w, bool hi)
 //   which side of y1 the quotient lies.
 // The residuals must not underflow: callers pass s >= 2^-64 (smaller block
 // scales are handled by multiplying x and s by 2^64).
-template <int FMAX>
+template <int FMAX, bool CLAMP>
 __device__ __forceinline__ float fp8_ro_quotient(float x, float s, float rs)
 {
     const float ax = fabsf(x);
@@ -546,13 +554,15 @@ __device__ __forceinline__ float fp8_ro_quotient(float x, float s, float rs)
     const float r = __builtin_fmaf(-y1, s, ax);
     uint32_t t = __float_as_uint(y1);
     t = (t - (r < 0.0f ? 1u : 0u)) | (r != 0.0f ? 1u : 0u);
-    const float yo = fminf(__uint_as_float(t), (float)FMAX);
+    const float yo = CLAMP ? fminf(__uint_as_float(t), (float)FMAX) : __uint_as_float(t);
     return __uint_as_float(__float_as_uint(yo) | (__float_as_uint(x) & 0x80000000u));
 }
 
 // Codes of the exact quotients x / s (scales as multipliers m = s), with x
-// and s both multiplied by k (an exact power of two).
-template <int FMT, int H>
+// and s both multiplied by k (an exact power of two).  CLAMP = false when
+// every quotient is known to round to at most the format's largest value
+// (see fp8_encode).
+template <int FMT, int H, bool CLAMP>
 __device__ __forceinline__ void fp8_quotient_codes(const float (&v)[32], const float (&sk)[H], float k,
                                                    uint32_t (&d)[8])
 {
@@ -564,10 +574,10 @@ __device__ __forceinline__ void fp8_quotient_codes(const float (&v)[32], const f
     for (int i = 0; i < 8; ++i) {
         const int h = H == 2 ? i / 4 : 0;
         const float* x = v + 4 * i;
-        const uint32_t w = f8_pair<FMT>(fp8_ro_quotient<FM>(x[0] * k, sk[h], rs[h]),
-                                        fp8_ro_quotient<FM>(x[1] * k, sk[h], rs[h]), 0u, false);
-        d[i] = f8_pair<FMT>(fp8_ro_quotient<FM>(x[2] * k, sk[h], rs[h]),
-                            fp8_ro_quotient<FM>(x[3] * k, sk[h], rs[h]), w, true);
+        const uint32_t w = f8_pair<FMT>(fp8_ro_quotient<FM, CLAMP>(x[0] * k, sk[h], rs[h]),
+                                        fp8_ro_quotient<FM, CLAMP>(x[1] * k, sk[h], rs[h]), any_word(), false);
+        d[i] = f8_pair<FMT>(fp8_ro_quotient<FM, CLAMP>(x[2] * k, sk[h], rs[h]),
+                            fp8_ro_quotient<FM, CLAMP>(x[3] * k, sk[h], rs[h]), w, true);
     }
 }
 
@@ -585,7 +595,7 @@ __device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale 
             float y[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(v[4 * i + j] * m, -FM), FM);
-            d[i] = f8_pair<FMT>(y[2], y[3], f8_pair<FMT>(y[0], y[1], 0u, false), true);
+            d[i] = f8_pair<FMT>(y[2], y[3], f8_pair<FMT>(y[0], y[1], any_word(), false), true);
         }
     } else {
         float s[H];
@@ -595,13 +605,19 @@ __device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale 
             s[h] = sc[h].zero ? 1.0f : sc[h].m;
             if constexpr (SC == kS32) tiny = tiny || (s[h] < 0x1p-64f);
         }
+        // FP32 scale: s = RN32(absmax / fmax) is normal or the block is zero,
+        // so |x| / s <= fmax / (1 - 2^-24), which rounds to fmax in both
+        // formats (the next code point up lies far beyond); the round-to-odd
+        // value stays below the first value that would overflow.  FP16
+        // scales (subnormal or clamped at 65504) need the clamp.
+        constexpr bool CL = SC != kS32;
         if (!tiny) {
-            fp8_quotient_codes<FMT, H>(v, s, 1.0f, d);
+            fp8_quotient_codes<FMT, H, CL>(v, s, 1.0f, d);
         } else {                              // tiny scale: x * 2^64 and s * 2^64 are exact
             float sk[H];
 #pragma unroll
             for (int h = 0; h < H; ++h) sk[h] = s[h] * 0x1p64f;
-            fp8_quotient_codes<FMT, H>(v, sk, 0x1p64f, d);
+            fp8_quotient_codes<FMT, H, CL>(v, sk, 0x1p64f, d);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) d[i] &= keep_mask(sc, i / 4);
@@ -641,7 +657,7 @@ __device__ __forceinline__ void mx_encode(const float (&v)[32], const EncScale (
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const float p = sc[H == 2 ? d / 2 : 0].m;         // 2^e as the conversion's scale operand
-        uint32_t w = 0u;
+        uint32_t w = any_word();                  // all four bytes are written
 #pragma unroll
         for (int b = 0; b < 4; ++b) w = fp4_enc(w, v[8 * d + 2 * b], v[8 * d + 2 * b + 1], p, b);
         D[d] = w;
