@@ -40,6 +40,10 @@ constexpr int kWavesPerGroup = 4;          // 256-thread workgroups, one tile pe
 // The byte / word selectors of these instructions must be literals; the
 // switches fold away once the callers' loops are unrolled.
 
+#ifndef RC_INT3_E8M0_SCALED_ENC
+#define RC_INT3_E8M0_SCALED_ENC 1
+#endif
+
 // An unspecified 32-bit value: the starting word of a code word whose bytes
 // (or 16-bit halves) are all overwritten by the conversions that follow, so
 // no register has to be cleared first.
@@ -394,12 +398,17 @@ __device__ __forceinline__ uint32_t int3_clamp_word(uint32_t w)
 // INT3 codes: E2M1 nibbles of x * m / 2 (m = fp32(1/s) or 2^-e): RNE, the
 // low code bit is the integer's parity below 2; clamped when a block may
 // exceed 3.
-template <int H>
+// E8M0 scales (P2): the multiplier 2^-e is a power of two, so the
+// conversion's own scale operand 2^(e+1) divides exactly and no multiply is
+// needed (e <= 126 for finite data, so the operand is finite).
+template <int H, bool P2>
 __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const EncScale (&sc)[H])
 {
     float r2[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) r2[h] = 0.5f * sc[h].m;                // exact
+    for (int h = 0; h < H; ++h)
+        r2[h] = (P2 && RC_INT3_E8M0_SCALED_ENC) ? __builtin_ldexpf(2.0f, (int)sc[h].bits - 127)
+                                                : 0.5f * sc[h].m;      // exact
     uint32_t N[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -407,7 +416,8 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float r = r2[H == 2 ? b / 2 : 0];
-            w = fp4_enc(w, v[8 * b + g] * r, v[8 * b + 4 + g] * r, 1.0f, b);
+            if constexpr (P2 && RC_INT3_E8M0_SCALED_ENC) w = fp4_enc(w, v[8 * b + g], v[8 * b + 4 + g], r, b);
+            else w = fp4_enc(w, v[8 * b + g] * r, v[8 * b + 4 + g] * r, 1.0f, b);
         }
         N[g] = w;
     }

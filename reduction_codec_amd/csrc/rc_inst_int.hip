@@ -1,5 +1,5 @@
 // INT4 / INT3 variants: FP16 scales on 16- and 64-element blocks, E8M0
-// scales on every block size; run-time stream count in the reduce.
+// scales on every block size; reduce unrolled for 2, 4 and 8 streams.
 #include "rc_inst.hpp"
 
 using namespace rc;

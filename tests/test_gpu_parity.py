@@ -405,7 +405,7 @@ def test_variant_unpack_bit_exact(name, odt):
 
 
 @pytest.mark.parametrize("name", VARIANTS)
-@pytest.mark.parametrize("k", [1, 2, 3, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 8])
 def test_variant_reduce_bit_exact(name, k):
     n = 2 * 2048 + 300
     say(f"case variant reduce {name} k={k}")
@@ -424,6 +424,32 @@ def test_variant_reduce_bit_exact(name, k):
     got = host_u8(buf)
     assert_same(got[:pb], ref, name)
     assert (got[pb:] == 0xA5).all()
+    assert_sums(sums.cpu().numpy(), ref_sum)
+
+
+@pytest.mark.parametrize("name", [n for n in VARIANTS if n.startswith(("int4_e8m0", "int3_e8m0"))])
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_int_e8m0_reduce_huge_block_exponents(name, k):
+    """E8M0 scales near the top of the exponent range (blocks of ~1e37, shared
+    exponent above 118) in the first tile only: the wave that holds them and
+    the waves that do not take different decode and encode paths; both must
+    match the oracle.  Sums stay finite."""
+    n = 3 * 2048 + 500
+    say(f"case e8m0 huge exponents {name} k={k}")
+    c_or = oracle.ALL_CODECS[name]
+    streams = []
+    for j in range(k):
+        r = np.random.default_rng(900 + 7 * j + k)
+        x = r.standard_normal(n).astype(np.float32)
+        for b in (0, 5, 6, 40, 63):                  # blocks of the first tile
+            x[32 * b:32 * b + 32] *= np.float32(1e37 / (k + 1))
+        x[32 * 7:32 * 7 + 32] *= np.float32(3e-39)   # and a denormal block beside them
+        streams.append(oracle.quantize_pack(c_or, x, dtype=oracle.DT_FP32))
+    ref, ref_sum = oracle.dequant_reduce_requant(c_or, streams, n, want_sum=True)
+    assert np.isfinite(ref_sum).all()
+    c = rca.ALL_CODECS[name]
+    out, sums = rca.dequant_reduce_requant([torch.from_numpy(s).to(DEV) for s in streams], c, n, sum_out=True)
+    assert_same(host_u8(out), ref, name)
     assert_sums(sums.cpu().numpy(), ref_sum)
 
 
