@@ -76,7 +76,10 @@
 extern "C" {
 #endif
 
-#define RC_ABI_VERSION 2
+/* 1: the four default codecs; 2: format, scale and block variants, the fused
+ * all-reduce emulation and the MXFP4 GEMV; 3: FP8 codes in two 1024-byte
+ * planes (packed FP8 data of version 2 reads differently). */
+#define RC_ABI_VERSION 3
 #define RC_TILE_ELEMS 2048
 #define RC_BLOCK_ELEMS 32
 #define RC_MAX_STREAMS 16

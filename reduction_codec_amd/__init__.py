@@ -61,6 +61,7 @@ def _all_codecs():
 
 ALL_CODECS = _all_codecs()
 
+ABI_VERSION = 3                       # RC_ABI_VERSION of include/rcodec.h
 _DTYPES = {torch.float32: DT_FP32, torch.float16: DT_FP16, torch.bfloat16: DT_BF16}
 _lib = None
 
@@ -96,6 +97,9 @@ def lib() -> ctypes.CDLL:
     l.rc_allreduce_emulate.argtypes = [Codec, i32, ctypes.POINTER(vp), i32, sz, i32, vp, vp, vp]
     l.rc_status_str.restype, l.rc_status_str.argtypes = ctypes.c_char_p, [i32]
     l.rc_abi_version.restype, l.rc_abi_version.argtypes = i32, []
+    if l.rc_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {l.rc_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}; rebuild the library")
     _lib = l
     return l
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert rca.lib().rc_abi_version() == 2
+    assert rca.lib().rc_abi_version() == 3 == rca.ABI_VERSION
 
 
 def test_enums_agree_with_oracle():
