@@ -19,7 +19,8 @@ the same workload).
 Extra modes:
   --table                               per-kernel table over all formats and
                                         sizes (--table-mib)
-  --summarize-pmc FETCH_DIR WRITE_DIR   turn two `rocprofv3 --pmc` runs of this
+  --summarize-pmc FETCH_DIR WRITE_DIR [SQ_DIR]
+                                        turn `rocprofv3 --pmc` runs of this
                                         script into profiles/traffic_*.json
 """
 import argparse
@@ -34,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+VALU_PEAK_GINST = 256 * 4 * 2.4 / 4          # 256 CUs x 4 SIMDs, a wave64 instruction per 4 cycles at 2.4 GHz
 METRIC = "codec GB/s (uncompressed bytes) and % of HBM peak, 64 MB INT3 quant+reduce"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_int3_64MiB.json")
 KERNEL_SOURCES = ["reduction_codec_amd/csrc/rc_device.hpp", "reduction_codec_amd/csrc/rc_kernels.hpp",
@@ -59,7 +61,9 @@ def parse_args():
     ap.add_argument("--fmt", default="int3", choices=["int3", "int4", "fp8", "mxfp4"])
     ap.add_argument("--sets", type=int, default=0, help="rotation buffer sets (0 = enough for 1 GiB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [SQ_DIR]: rocprofv3 --pmc runs of FETCH_SIZE, WRITE_SIZE "
+                         "and (optionally) SQ_INSTS_VALU")
     ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
                     help="per-kernel duration table from a rocprofv3 --kernel-trace results database")
     ap.add_argument("--table", action="store_true",
@@ -86,9 +90,11 @@ def _read_counter_rows(d: str):
     return rows
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str):
+def summarize_pmc(fetch_dir: str, write_dir: str, sq_dir: str | None = None):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by
-    what the same counters read for the plain copy kernel of known size."""
+    what the same counters read for the plain copy kernel of known size; with
+    sq_dir (a run that collected SQ_INSTS_VALU), also the wave64 VALU
+    instructions each launch issues."""
     def per_kernel(d, counter):
         acc = {}
         for r in _read_counter_rows(d):
@@ -99,6 +105,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    valu = per_kernel(sq_dir, "SQ_INSTS_VALU") if sq_dir else {}
 
     def find(table, key):
         hits = [v for k, v in table.items() if key in k]
@@ -116,6 +123,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
             continue
         out["kernels"][key] = {"fetch_kib": f, "write_kib": w,
                                "bytes": f * 1024.0 * fscale + w * 1024.0 * wscale}
+        v = find(valu, key)
+        if v is not None:
+            out["kernels"][key]["valu_insts"] = v
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -136,16 +146,21 @@ def summarize_trace(db_path: str) -> int:
     return 0
 
 
-def traffic_for(kernel_key: str):
+def counters_for(kernel_key: str) -> dict:
+    """The stored counter figures of one kernel, or {} when they were taken
+    from other kernel sources than the ones in this tree."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("kernel_source_sha") != kernel_source_hash():
-        return None
-    k = t.get("kernels", {}).get(kernel_key)
-    return k["bytes"] if k else None
+        return {}
+    return t.get("kernels", {}).get(kernel_key) or {}
+
+
+def traffic_for(kernel_key: str):
+    return counters_for(kernel_key).get("bytes")
 
 
 # -------------------------------------------------------------- bench ----
@@ -153,6 +168,9 @@ def traffic_for(kernel_key: str):
 def main():
     args = parse_args()
     if args.summarize_pmc:
+        if len(args.summarize_pmc) not in (2, 3):
+            sys.stderr.write("--summarize-pmc takes FETCH_DIR WRITE_DIR [SQ_DIR]\n")
+            return 2
         summarize_pmc(*args.summarize_pmc)
         return 0
     if args.summarize_trace:
@@ -279,6 +297,15 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_key),
             "kernel": f"{dom_key}<{args.fmt}" + (f", K={K}>" if dom_key == "reduce_kernel" else ", bf16>"),
             "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
+    valu = counters_for(dom_key).get("valu_insts")
+    if valu:
+        # the same launch against the vector-ALU issue limit: wave64 VALU
+        # instructions (SQ_INSTS_VALU) per launch / launch time, against one
+        # instruction per 4 cycles on each of 256 x 4 SIMDs at 2.4 GHz
+        rate = valu / (dom_ms * 1e-3) / 1e9
+        roof["alu"] = {"valu_insts_per_launch": int(valu), "achieved": round(rate, 1),
+                       "peak": VALU_PEAK_GINST, "unit": "G wave64 VALU instructions/s",
+                       "frac": round(rate / VALU_PEAK_GINST, 4)}
 
     cpu = None
     if not args.no_cpu:
