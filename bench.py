@@ -372,6 +372,14 @@ def table(args):
         x0 = torch.from_numpy(datagen.bf16_student4(2 * n, 0).view(np.int16)).view(torch.bfloat16).to(dev)
         names = sorted(rca.ALL_CODECS) if args.table_codecs == "all" else args.table_codecs.split(",")
         ks = [int(v) for v in args.table_k.split(",")]
+        # the achievable-bandwidth reference at this size: a plain copy of the bf16 message
+        csets = max(1, -(-(1 << 30) // (4 * n)))
+        cbufs = [(x0.clone(), torch.empty_like(x0)) for _ in range(csets)]
+        ms = timed(lambda i: rca.copy(cbufs[i % csets][1], cbufs[i % csets][0]))
+        g = 4 * n / (ms * 1e-3) / 1e9
+        print(f"| {mib} | - | copy bf16 (reference) | {ms * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
+              f"{2 * n / (ms * 1e-3) / 1e9:.0f} |", flush=True)
+        del cbufs
         for fmt in names:
             codec = rca.CODECS[fmt] if fmt in rca.CODECS else rca.ALL_CODECS[fmt]
             pb = rca.packed_bytes(codec, n)
@@ -556,7 +564,13 @@ def cpu_baseline(args, host, n, K):
         if dt >= 1.5 or reps >= 50:
             break
     unc = reps * (2 * ns + K * 2 * ns)
-    return {"value": round(unc / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(unc / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": model,
             "sample": f"{sample_tiles} tiles ({ns} elements) of the same message and peers, {reps} repetitions of "
                       f"quantize + {K}-stream reduce, tile ranges over {threads} threads, {dt:.2f} s wall"}
 
