@@ -40,9 +40,6 @@ constexpr int kWavesPerGroup = 4;          // 256-thread workgroups, one tile pe
 // The byte / word selectors of these instructions must be literals; the
 // switches fold away once the callers' loops are unrolled.
 
-#ifndef RC_INT3_E8M0_SCALED_ENC
-#define RC_INT3_E8M0_SCALED_ENC 1
-#endif
 
 // An unspecified 32-bit value: the starting word of a code word whose bytes
 // (or 16-bit halves) are all overwritten by the conversions that follow, so
@@ -407,8 +404,8 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
     float r2[H];
 #pragma unroll
     for (int h = 0; h < H; ++h)
-        r2[h] = (P2 && RC_INT3_E8M0_SCALED_ENC) ? __builtin_ldexpf(2.0f, (int)sc[h].bits - 127)
-                                                : 0.5f * sc[h].m;      // exact
+        r2[h] = P2 ? __builtin_ldexpf(2.0f, (int)sc[h].bits - 127)   // 2^(e+1), the operand
+                   : 0.5f * sc[h].m;                                  // r/2, exact
     uint32_t N[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -416,7 +413,7 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float r = r2[H == 2 ? b / 2 : 0];
-            if constexpr (P2 && RC_INT3_E8M0_SCALED_ENC) w = fp4_enc(w, v[8 * b + g], v[8 * b + 4 + g], r, b);
+            if constexpr (P2) w = fp4_enc(w, v[8 * b + g], v[8 * b + 4 + g], r, b);
             else w = fp4_enc(w, v[8 * b + g] * r, v[8 * b + 4 + g] * r, 1.0f, b);
         }
         N[g] = w;
