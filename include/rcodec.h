@@ -57,7 +57,10 @@
  * Conventions shared by every entry point:
  *   - Pointers named in/out/ins[k]/sum_out are device pointers (HIP global
  *     memory), 16-byte aligned; the caller owns all of them.  Inputs and
- *     outputs must not overlap.
+ *     outputs must not overlap, with two exceptions for in-place use: the
+ *     `out` of rc_dequant_reduce_requant may be exactly one of ins[], and the
+ *     `out` of rc_allreduce_emulate exactly one of msgs[] (each tile is read
+ *     in full before anything of that tile is written).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     there and completes asynchronously; the library never synchronizes,
  *     allocates nothing and keeps no state, so calls are thread-safe.

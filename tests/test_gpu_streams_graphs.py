@@ -1,4 +1,4 @@
-"""The C ABI on a caller's stream and under HIP graph capture.
+"""The C ABI on a caller's stream, under HIP graph capture, and in place.
 
 Every entry point takes the caller's stream and allocates nothing, so the
 whole path can run on a side stream and be captured into a graph.  These
@@ -6,7 +6,8 @@ tests check both against the CPU oracle: work launched on a non-default
 stream, and a captured quantize -> 4-stream reduce -> unpack pipeline
 replayed several times with new inputs written eagerly between the replays
 (each replay must compute from the inputs it finds, and no replay may reuse
-an earlier result).
+an earlier result); and the two in-place uses the header allows (the reduce
+into its first stream, the all-reduce emulation into one of its messages).
 """
 import numpy as np
 import pytest
@@ -107,3 +108,31 @@ def test_graph_replays_follow_their_inputs(fmt):
         assert np.array_equal(p0.cpu().numpy(), ref_p0), f"replay {round_}: packed message"
         assert np.array_equal(out.cpu().numpy(), ref_out), f"replay {round_}: reduced stream"
         assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref_y), f"replay {round_}: unpack"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_reduce_in_place_into_the_first_stream(fmt):
+    """rc_dequant_reduce_requant with out == ins[0]: the header allows it
+    (every tile is read in full before it is written)."""
+    print(f"case in-place reduce {fmt}", flush=True)
+    c = oracle.CODECS[fmt]
+    streams = [oracle.quantize_pack(c, message(300 + j), dtype=oracle.DT_BF16) for j in range(4)]
+    ref, _ = oracle.dequant_reduce_requant(c, streams, N)
+    devs = [torch.from_numpy(s).to(DEV) for s in streams]
+    rca.dequant_reduce_requant(devs, rca.CODECS[fmt], N, out=devs[0])
+    torch.cuda.synchronize()
+    assert np.array_equal(devs[0].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("two_shot", [True, False])
+def test_allreduce_emulate_in_place(fmt, two_shot):
+    """rc_allreduce_emulate with out == msgs[1] (the usual in-place
+    all-reduce): same result as into a separate buffer."""
+    print(f"case in-place allreduce {fmt} two_shot={two_shot}", flush=True)
+    msgs = [message(400 + j) for j in range(3)]
+    ref, _ = oracle.allreduce_emulate(oracle.CODECS[fmt], msgs, oracle.DT_BF16, two_shot=two_shot)
+    devs = [bf16_dev(m) for m in msgs]
+    rca.allreduce_emulate(devs, rca.CODECS[fmt], two_shot=two_shot, out=devs[1])
+    torch.cuda.synchronize()
+    assert np.array_equal(devs[1].view(torch.int16).cpu().numpy().view(np.uint16), ref)
