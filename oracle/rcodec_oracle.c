@@ -256,7 +256,7 @@ int rco_int_mag_recip(float v_abs, float r, int qmax)
 {
     const float y = v_abs * r;
     const double yd = (double)y;
-    if (yd >= qmax + 0.5) return qmax;                 /* RNE, then clamp */
+    if (!(yd < qmax + 0.5)) return qmax;               /* RNE, then clamp (NaN: qmax) */
     const int k = (int)floor(yd);
     const double frac = yd - (double)k;
     int m;
@@ -412,7 +412,7 @@ static float block_absmax(const float *v, int len)
  * power of two, held exactly in a double), ties to even, clamped to qmax. */
 static int int_mag_exact(double y, int qmax)
 {
-    if (y >= qmax + 0.5) return qmax;
+    if (!(y < qmax + 0.5)) return qmax;                /* NaN: qmax */
     double k = floor(y), frac = y - k;        /* both exact */
     int m = (int)k;
     if (frac > 0.5 || (frac == 0.5 && m % 2 == 1)) m += 1;
