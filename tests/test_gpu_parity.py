@@ -504,3 +504,56 @@ def test_mxfp4_gemv_weight_4096x4096_sampled_rows():
     sub = np.concatenate([ph[2 * r * tb:(2 * r + 2) * tb] for r in pick])
     ref = oracle.mxfp4_gemv(sub, len(pick), cols, x, x_dtype=oracle.DT_BF16)
     assert_same(y[pick], ref, "gemv sampled rows")
+
+
+# ---------------------------------------------------------- beyond 4 GiB ----
+
+def _big_message(n: int, seed: int) -> np.ndarray:
+    """n bf16 values: one seeded Student-t chunk repeated, each repetition
+    with different low mantissa bits, so no two regions of the message are
+    alike (an access that lands in the wrong 4 GiB window shows)."""
+    chunk = datagen.bf16_student4(1 << 24, seed)                       # 8M values
+    x = np.empty(n, dtype=np.uint16)
+    for r, i in enumerate(range(0, n, chunk.size)):
+        m = min(chunk.size, n - i)
+        np.bitwise_xor(chunk[:m], np.uint16(1 + r % 127), out=x[i:i + m])
+    return x
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt", ["int3", "fp8"])
+def test_message_beyond_4gib(fmt):
+    """A bf16 message of 2^31 + 3 tiles + 777 elements (4 GiB + of input and of
+    unpacked output; 2.4 GB of FP8 codes): quantize, a 2-stream reduce and
+    unpack, checked against the oracle on tiles around the 2^30 and 2^31
+    element (2 GiB and 4 GiB byte) boundaries, random tiles and the ragged
+    last tile."""
+    n = (1 << 31) + 3 * 2048 + 777
+    say(f"case beyond 4 GiB fmt={fmt} n={n}")
+    c, oc = rca.CODECS[fmt], oracle.CODECS[fmt]
+    tb = oracle.tile_bytes(oc)
+    tiles = -(-n // 2048)
+    xa, xb = _big_message(n, 31), _big_message(n, 32)
+    pa = rca.quantize_pack(torch.from_numpy(xa.view(np.int16)).view(torch.bfloat16).to(DEV), c)
+    xbd = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    pb_ = rca.quantize_pack(xbd, c)
+    del xbd
+    out, _ = rca.dequant_reduce_requant([pa, pb_], c, n)
+    y = rca.unpack_dequant(out, c, n, torch.bfloat16)
+    torch.cuda.synchronize()
+    t2g, t4g = (1 << 30) // 2048, (1 << 31) // 2048
+    picks = {0, t2g - 1, t2g, t4g - 1, t4g, t4g + 1, tiles - 1}
+    picks.update(int(t) for t in np.random.default_rng(5).integers(0, tiles, 12))
+    for t in sorted(picks):
+        lo, cnt = t * 2048, min(2048, n - t * 2048)
+        ra = oracle.quantize_pack(oc, xa[lo:lo + cnt], dtype=oracle.DT_BF16)
+        rb = oracle.quantize_pack(oc, xb[lo:lo + cnt], dtype=oracle.DT_BF16)
+        assert np.array_equal(host_u8(pa[t * tb:(t + 1) * tb]), ra), f"quantize tile {t}"
+        assert np.array_equal(host_u8(pb_[t * tb:(t + 1) * tb]), rb), f"quantize tile {t} (stream b)"
+        ro, _ = oracle.dequant_reduce_requant(oc, [ra, rb], cnt)
+        assert np.array_equal(host_u8(out[t * tb:(t + 1) * tb]), ro), f"reduce tile {t}"
+        ry = oracle.unpack_dequant(oc, ro, cnt, oracle.DT_BF16)
+        got = y[lo:lo + cnt].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ry), f"unpack tile {t}"
+    del pa, pb_, out, y
+    torch.cuda.empty_cache()
