@@ -40,15 +40,6 @@ constexpr int kWavesPerGroup = 4;          // 256-thread workgroups, one tile pe
 // The byte / word selectors of these instructions must be literals; the
 // switches fold away once the callers' loops are unrolled.
 
-
-// An unspecified 32-bit value: the starting word of a code word whose bytes
-// (or 16-bit halves) are all overwritten by the conversions that follow, so
-// no register has to be cleared first.
-__device__ __forceinline__ uint32_t any_word()
-{
-    return __builtin_nondeterministic_value(0u);
-}
-
 // Two binary32 -> two E2M1 codes (RNE, saturating at 6, sign kept) of
 // a / 2^k and b / 2^k, 2^k = the power-of-two part of `scale`; a goes to the
 // low nibble of byte `sel` of `old`, b to its high nibble.
@@ -409,12 +400,14 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
     uint32_t N[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        uint32_t w = any_word();                  // all four bytes are written
+        uint32_t w = 0u;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float r = r2[H == 2 ? b / 2 : 0];
-            if constexpr (P2) w = fp4_enc(w, v[8 * b + g], v[8 * b + 4 + g], r, b);
-            else w = fp4_enc(w, v[8 * b + g] * r, v[8 * b + 4 + g] * r, 1.0f, b);
+            const float x0 = P2 ? v[8 * b + g] : v[8 * b + g] * r, x1 = P2 ? v[8 * b + 4 + g] : v[8 * b + 4 + g] * r;
+            // the first conversion starts from x0's own bits: every byte of w
+            // is written by the four conversions, and no register is cleared
+            w = fp4_enc(b == 0 ? __float_as_uint(x0) : w, x0, x1, P2 ? r : 1.0f, b);
         }
         N[g] = w;
     }
@@ -480,8 +473,9 @@ __device__ __forceinline__ void int4_encode(const float (&v)[32], const EncScale
     for (int d = 0; d < 4; ++d) {
         const float r = r9[H == 2 ? d / 2 : 0];
         const float* y = v + 8 * d;
-        xe[d] = fp8_pair(y[4] * r, y[6] * r, fp8_pair(y[0] * r, y[2] * r, any_word(), false), true);
-        xo[d] = fp8_pair(y[5] * r, y[7] * r, fp8_pair(y[1] * r, y[3] * r, any_word(), false), true);
+        const float e0 = y[0] * r, o0 = y[1] * r;   // first conversions start from their own bits
+        xe[d] = fp8_pair(y[4] * r, y[6] * r, fp8_pair(e0, y[2] * r, __float_as_uint(e0), false), true);
+        xo[d] = fp8_pair(y[5] * r, y[7] * r, fp8_pair(o0, y[3] * r, __float_as_uint(o0), false), true);
     }
     bool clamp = sc[0].clamp;
     if constexpr (H == 2) clamp = clamp || sc[1].clamp;
@@ -581,8 +575,9 @@ __device__ __forceinline__ void fp8_quotient_codes(const float (&v)[32], const f
     for (int i = 0; i < 8; ++i) {
         const int h = H == 2 ? i / 4 : 0;
         const float* x = v + 4 * i;
-        const uint32_t w = f8_pair<FMT>(fp8_ro_quotient<FM, CLAMP>(x[0] * k, sk[h], rs[h]),
-                                        fp8_ro_quotient<FM, CLAMP>(x[1] * k, sk[h], rs[h]), any_word(), false);
+        const float q0 = fp8_ro_quotient<FM, CLAMP>(x[0] * k, sk[h], rs[h]);
+        const uint32_t w = f8_pair<FMT>(q0, fp8_ro_quotient<FM, CLAMP>(x[1] * k, sk[h], rs[h]),
+                                        __float_as_uint(q0), false);     // starts from q0's own bits
         d[i] = f8_pair<FMT>(fp8_ro_quotient<FM, CLAMP>(x[2] * k, sk[h], rs[h]),
                             fp8_ro_quotient<FM, CLAMP>(x[3] * k, sk[h], rs[h]), w, true);
     }
@@ -602,7 +597,7 @@ __device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale 
             float y[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(v[4 * i + j] * m, -FM), FM);
-            d[i] = f8_pair<FMT>(y[2], y[3], f8_pair<FMT>(y[0], y[1], any_word(), false), true);
+            d[i] = f8_pair<FMT>(y[2], y[3], f8_pair<FMT>(y[0], y[1], __float_as_uint(y[0]), false), true);
         }
     } else {
         float s[H];
@@ -664,7 +659,7 @@ __device__ __forceinline__ void mx_encode(const float (&v)[32], const EncScale (
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const float p = sc[H == 2 ? d / 2 : 0].m;         // 2^e as the conversion's scale operand
-        uint32_t w = any_word();                  // all four bytes are written
+        uint32_t w = __float_as_uint(v[8 * d]);   // all four bytes are overwritten
 #pragma unroll
         for (int b = 0; b < 4; ++b) w = fp4_enc(w, v[8 * d + 2 * b], v[8 * d + 2 * b + 1], p, b);
         D[d] = w;
