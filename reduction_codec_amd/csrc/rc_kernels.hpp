@@ -291,6 +291,14 @@ __device__ __forceinline__ void widen_chunks(const u32x4 (&c)[CPB], float (&v)[3
     }
 }
 
+// Occupancy targets of the quantize kernel: fp32 input needs 36 KiB of LDS
+// per workgroup (4 waves per SIMD fit); FP8 codes from 16-bit input run at 7
+// (its exact-quotient encoder then holds its values without spilling:
+// measured 3 % faster than 8 at 64 MiB); the others at RC_QUANT_WAVES.
+template <int FMT, int DT> struct QuantWaves {
+    static constexpr int v = DT == kF32 ? 4 : ((FMT == kFp8 || FMT == kBf8) ? 7 : RC_QUANT_WAVES);
+};
+
 // One wave quantizes one whole tile per iteration (fp32 input: the padded
 // LDS rows of four waves take 36 KiB, so at most 4 waves per SIMD fit).
 // With RC_QUANT_LDS the
@@ -301,7 +309,7 @@ __device__ __forceinline__ void widen_chunks(const u32x4 (&c)[CPB], float (&v)[3
 // (no in-wave prefetch).  The partial last tile, if any, is done after the
 // loop by the wave whose walk would reach it.
 template <int FMT, int SC, int BL, int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 ? 4 : RC_QUANT_WAVES)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QuantWaves<FMT, DT>::v)))
 void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict__ out, size_t tiles)
 {
     constexpr int ES = (DT == kF32) ? 4 : 2;
