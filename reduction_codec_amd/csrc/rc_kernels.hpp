@@ -360,8 +360,18 @@ void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict_
 template <int FMT> struct ReduceBatch {
     static constexpr int v = (FMT == kFp8 || FMT == kBf8) ? RC_FP8_REDUCE_BATCH : RC_REDUCE_BATCH;
 };
-template <int FMT> struct ReduceWaves {
-    static constexpr int v = (FMT == kFp8 || FMT == kBf8) ? RC_FP8_REDUCE_WAVES : RC_REDUCE_WAVES;
+// Occupancy target of the reduce (waves per SIMD; 8 = at most 64 VGPRs).
+// At 8, the INT kernels with two scales per lane or shared across a lane
+// pair (16- and 64-element blocks) and with E8M0 scales spill registers
+// once more than four streams are unrolled or k is a run-time count; they
+// run at 6 (measured 1.2-1.5x faster at k = 8), INT4 with E8M0 scales at 7
+// below that.  FP8 runs at RC_FP8_REDUCE_WAVES.
+template <int FMT, int SC, int BL, int K> struct ReduceWaves {
+    static constexpr bool kInt = FMT == kInt3 || FMT == kInt4;
+    static constexpr bool kVar = BL != 32 || SC == kSE8;
+    static constexpr int v = (FMT == kFp8 || FMT == kBf8) ? RC_FP8_REDUCE_WAVES
+                           : (kInt && kVar && (K == 0 || K > 4)) ? 6
+                           : (FMT == kInt4 && SC == kSE8) ? 7 : RC_REDUCE_WAVES;
 };
 
 // acc = the K streams' decoded values of the lane's 32 elements of `tile`,
@@ -419,7 +429,7 @@ __device__ __forceinline__ void store_sums(float* __restrict__ sum_out, size_t t
 // covered by the other waves of the SIMD.  The partial last tile (if any)
 // is done after the loop by the wave whose walk would reach it.
 template <int FMT, int SC, int BL, int K>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ReduceWaves<FMT>::v)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ReduceWaves<FMT, SC, BL, K>::v)))
 void reduce_kernel(StreamPtrs ins, int k, size_t n, uint8_t* __restrict__ out, float* __restrict__ sum_out,
                    size_t tiles)
 {
