@@ -22,7 +22,9 @@
  *                   e of block b at bit 64b + 32*((e/2)%2) + 4*((e/2)/2) +
  *                   2*(e%2); q1w plane = bytes [512,768): sign of tile element
  *                   i at bit i; fp16 scale of block b at 768 + 2b.
- *   FP8 (2304 B):   byte i = E4M3 code; fp32 scale of block b at 2048 + 4b.
+ *   FP8 (2304 B):   E4M3 / E5M2 codes in two planes: element e < 16 of the
+ *                   32-element group g at byte 16g + e, element e >= 16 at
+ *                   1024 + 16g + (e - 16); fp32 scale of block b at 2048 + 4b.
  *   MXFP4 (1088 B): nibble i of bytes [0,1024) = E2M1 code;
  *                   E8M0 scale byte of block b at 1024 + b.
  * All planes are little-endian bit streams (bit j of a plane is bit j%8 of
