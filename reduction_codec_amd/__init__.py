@@ -118,6 +118,15 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _mine(t: torch.Tensor, stream) -> torch.Tensor:
+    """A tensor this module allocated on the current stream for work enqueued
+    on `stream`: tell torch's caching allocator, so the memory is not handed
+    out again before that stream has finished with it."""
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
 def _check_dev(t: torch.Tensor, name: str):
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
@@ -147,7 +156,7 @@ def quantize_pack(x: torch.Tensor, codec, out: torch.Tensor | None = None, strea
         raise ValueError(f"unsupported input dtype {x.dtype}")
     n = x.numel()
     if out is None:
-        out = torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=x.device)
+        out = _mine(torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=x.device), stream)
     _check_dev(out, "out")
     if out.numel() < packed_bytes(c, n) or out.dtype != torch.uint8:
         raise ValueError("out must be a uint8 tensor of packed_bytes(codec, n) bytes")
@@ -166,7 +175,7 @@ def unpack_dequant(packed: torch.Tensor, codec, n: int, dtype: torch.dtype = tor
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported output dtype {dtype}")
     if out is None:
-        out = torch.empty(n, dtype=dtype, device=packed.device)
+        out = _mine(torch.empty(n, dtype=dtype, device=packed.device), stream)
     _check_dev(out, "out")
     if out.numel() < n or out.dtype != dtype:
         raise ValueError("out must hold n elements of dtype")
@@ -191,7 +200,7 @@ def dequant_reduce_requant(streams, codec, n: int, out: torch.Tensor | None = No
             raise ValueError(f"streams[{j}] is shorter than packed_bytes(codec, n)")
     dev = streams[0].device
     if out is None:
-        out = torch.empty(need, dtype=torch.uint8, device=dev)
+        out = _mine(torch.empty(need, dtype=torch.uint8, device=dev), stream)
     _check_dev(out, "out")
     sums = None
     if isinstance(sum_out, torch.Tensor):
@@ -200,7 +209,7 @@ def dequant_reduce_requant(streams, codec, n: int, out: torch.Tensor | None = No
         if sums.dtype != torch.float32 or sums.numel() < n:
             raise ValueError("sum_out must hold n float32 values")
     elif sum_out:
-        sums = torch.empty(n, dtype=torch.float32, device=dev)
+        sums = _mine(torch.empty(n, dtype=torch.float32, device=dev), stream)
     ptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in streams])
     _ok(lib().rc_dequant_reduce_requant(c, ptrs, k, n, out.data_ptr(),
                                         sums.data_ptr() if sums is not None else None, _stream(stream)),
@@ -227,7 +236,7 @@ def allreduce_emulate(msgs, codec, two_shot: bool = True, out: torch.Tensor | No
         if m.dtype != dt or m.numel() != n:
             raise ValueError("all messages need the same dtype and length")
     if out is None:
-        out = torch.empty(n, dtype=dt, device=msgs[0].device)
+        out = _mine(torch.empty(n, dtype=dt, device=msgs[0].device), stream)
     _check_dev(out, "out")
     if out.dtype != dt or out.numel() < n:
         raise ValueError("out must hold n elements of the messages' dtype")
@@ -238,7 +247,7 @@ def allreduce_emulate(msgs, codec, two_shot: bool = True, out: torch.Tensor | No
         if packed.numel() < packed_bytes(c, n) or packed.dtype != torch.uint8:
             raise ValueError("packed_out must be a uint8 tensor of packed_bytes(codec, n) bytes")
     elif packed_out:
-        packed = torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=msgs[0].device)
+        packed = _mine(torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=msgs[0].device), stream)
     ptrs = (ctypes.c_void_p * k)(*[m.data_ptr() for m in msgs])
     _ok(lib().rc_allreduce_emulate(c, _DTYPES[dt], ptrs, k, n, 1 if two_shot else 0, out.data_ptr(),
                                    packed.data_ptr() if packed is not None else None, _stream(stream)),
@@ -259,7 +268,7 @@ def mxfp4_gemv(w_packed: torch.Tensor, rows: int, cols: int, x: torch.Tensor, ou
     if out_dtype not in _DTYPES:
         raise ValueError(f"unsupported output dtype {out_dtype}")
     if out is None:
-        out = torch.empty(rows, dtype=out_dtype, device=x.device)
+        out = _mine(torch.empty(rows, dtype=out_dtype, device=x.device), stream)
     _check_dev(out, "out")
     if out.dtype != out_dtype or out.numel() < rows:
         raise ValueError("out must hold rows values of out_dtype")

@@ -136,3 +136,25 @@ def test_allreduce_emulate_in_place(fmt, two_shot):
     rca.allreduce_emulate(devs, rca.CODECS[fmt], two_shot=two_shot, out=devs[1])
     torch.cuda.synchronize()
     assert np.array_equal(devs[1].view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_stream_argument_without_switching_streams(fmt):
+    """Work enqueued on a side stream through the `stream` argument only (the
+    current stream stays the default one): outputs the binding allocates are
+    recorded on the side stream and come out equal to the oracle's."""
+    print(f"case stream argument {fmt}", flush=True)
+    x = message(61)
+    peers = [oracle.quantize_pack(oracle.CODECS[fmt], message(70 + j), dtype=oracle.DT_BF16) for j in range(3)]
+    ref_p0, ref_out, ref_y = oracle_pipeline(fmt, x, peers)
+    side = torch.cuda.Stream(device=DEV)
+    xd = bf16_dev(x)
+    pd = [torch.from_numpy(p).to(DEV) for p in peers]
+    side.wait_stream(torch.cuda.current_stream())
+    p0 = rca.quantize_pack(xd, rca.CODECS[fmt], stream=side)
+    out, _ = rca.dequant_reduce_requant([p0] + pd, rca.CODECS[fmt], N, stream=side)
+    y = rca.unpack_dequant(out, rca.CODECS[fmt], N, torch.bfloat16, stream=side)
+    side.synchronize()
+    assert np.array_equal(p0.cpu().numpy(), ref_p0)
+    assert np.array_equal(out.cpu().numpy(), ref_out)
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref_y)
