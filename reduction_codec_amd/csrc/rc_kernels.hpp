@@ -264,13 +264,14 @@ struct TileWalk {
     int lane, w;
 };
 
+template <int W = kWavesPerGroup>
 __device__ __forceinline__ TileWalk tile_walk()
 {
     TileWalk t;
-    t.w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    t.w = W == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     t.lane = lane_id();
-    t.first = (size_t)blockIdx.x * kWavesPerGroup + (size_t)t.w;
-    t.stride = (size_t)gridDim.x * kWavesPerGroup;
+    t.first = (size_t)blockIdx.x * W + (size_t)t.w;
+    t.stride = (size_t)gridDim.x * W;
     return t;
 }
 
@@ -366,6 +367,19 @@ template <int FMT> struct ReduceBatch {
 // once more than four streams are unrolled or k is a run-time count; they
 // run at 6 (measured 1.2-1.5x faster at k = 8), INT4 with E8M0 scales at 7
 // below that.  FP8 runs at RC_FP8_REDUCE_WAVES.
+// Waves per workgroup of the reduce.  INT codecs whose tiles are whole
+// 128-byte lines run one-wave workgroups: a freed wave slot is refilled at
+// once, which shortens the ramp and the drain of these ALU-bound kernels
+// (measured at 64 MiB: INT3 4 streams -6 %, 2 streams -12 %; 1 GiB -5 %).
+// Tiles that are not whole lines (MXFP4's 1088 B, the E8M0 and 64-block INT
+// variants) keep four-wave groups: one-wave groups deal neighbouring tiles
+// to different XCDs, which then both fetch the line the two tiles share
+// (MXFP4 measured 7-12 % slower).
+template <int FMT, int SC, int BL> struct ReduceGroupWaves {
+    static constexpr int v = (FMT == kInt3 || FMT == kInt4) && TileGeom<FMT, SC, BL>::bytes % 128 == 0
+                                 ? 1 : kWavesPerGroup;
+};
+
 template <int FMT, int SC, int BL, int K> struct ReduceWaves {
     static constexpr bool kInt = FMT == kInt3 || FMT == kInt4;
     static constexpr bool kVar = BL != 32 || SC == kSE8;
@@ -434,7 +448,7 @@ void reduce_kernel(StreamPtrs ins, int k, size_t n, uint8_t* __restrict__ out, f
                    size_t tiles)
 {
     constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
-    const TileWalk tw = tile_walk();
+    const TileWalk tw = tile_walk<ReduceGroupWaves<FMT, SC, BL>::v>();
     const uint32_t lane = (uint32_t)tw.lane;
     const size_t full = n / kTile;
     if (sum_out) {
@@ -779,12 +793,12 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
 // workgroups per compute unit (1 GiB of bf16 input on 256 CUs; measured
 // faster there than a 4x smaller grid walking 4 tiles per wave); beyond that
 // each wave walks several tiles.
-static inline dim3 tile_grid(size_t tiles)
+static inline dim3 tile_grid(size_t tiles, int waves = kWavesPerGroup)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const size_t groups = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    const size_t cap = (size_t)RC_GROUPS_PER_CU * (size_t)(cus > 0 ? cus : 256);
+    const size_t groups = (tiles + waves - 1) / waves;
+    const size_t cap = (size_t)RC_GROUPS_PER_CU * (size_t)(cus > 0 ? cus : 256) * (size_t)(kWavesPerGroup / waves);
     return dim3((unsigned)(groups < cap ? groups : cap));
 }
 
@@ -818,7 +832,8 @@ template <int FMT, int SC, int BL, int K>
 static hipError_t launch_reduce_k(const StreamPtrs& p, int k, size_t n, void* out, float* sum, hipStream_t st)
 {
     const size_t tiles = (n + kTile - 1) / kTile;
-    hipLaunchKernelGGL((reduce_kernel<FMT, SC, BL, K>), tile_grid(tiles), dim3(256), 0, st, p, k, n,
+    constexpr int W = ReduceGroupWaves<FMT, SC, BL>::v;
+    hipLaunchKernelGGL((reduce_kernel<FMT, SC, BL, K>), tile_grid(tiles, W), dim3(64 * W), 0, st, p, k, n,
                        static_cast<uint8_t*>(out), sum, tiles);
     return hipGetLastError();
 }
