@@ -74,6 +74,13 @@ constexpr int kNT = 2;                              // aux bits: nt
 // 2-4 % faster than nt alone there (and slower for the packed outputs of
 // quantize and reduce, and for the fused all-reduce's output rows).
 constexpr int kRowStore = 18;
+// Packed tiles read by unpack: with the 3- and 4-bit formats (at most
+// 0.5625 packed bytes per element, against 2-4 bytes written) plain loads
+// beat nt ones from about 128 MiB of bf16 output on (INT3 at 1 GiB: 243 ->
+// 215 us), and lose 4-6 % below 96 MiB; FP8 keeps nt loads at every size.
+// Quantize and reduce keep nt loads (plain ones measured 2-9 % slower).
+constexpr int kPlainLoad = 0;
+constexpr size_t kUnpackPlainLoadTiles = size_t(1) << 16;
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 __device__ __forceinline__ Rsrc span_rsrc(const void* base, size_t off, uint32_t bytes)
@@ -83,22 +90,22 @@ __device__ __forceinline__ Rsrc span_rsrc(const void* base, size_t off, uint32_t
 }
 
 // The per-lane code words of 32 elements, read from a stream's tile.
-template <int FMT>
+template <int FMT, int AUX = kNT>
 __device__ __forceinline__ LaneCodes<FMT> load_codes_buf(Rsrc r, uint32_t lane)
 {
     LaneCodes<FMT> c;
     if constexpr (FMT == kInt3) {
-        const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8u, 0, kNT);
+        const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8u, 0, AUX);
         c.w0 = q.x;
         c.w1 = q.y;
-        c.h = __builtin_amdgcn_raw_buffer_load_b32(r, 512u + lane * 4u, 0, kNT);
+        c.h = __builtin_amdgcn_raw_buffer_load_b32(r, 512u + lane * 4u, 0, AUX);
     } else if constexpr (FMT == kFp8 || FMT == kBf8) {
-        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, kNT);
-        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(r, 1024u + lane * 16u, 0, kNT);
+        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, AUX);
+        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(r, 1024u + lane * 16u, 0, AUX);
         c.d[0] = d0.x; c.d[1] = d0.y; c.d[2] = d0.z; c.d[3] = d0.w;
         c.d[4] = d1.x; c.d[5] = d1.y; c.d[6] = d1.z; c.d[7] = d1.w;
     } else {
-        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, kNT);
+        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16u, 0, AUX);
         c.d[0] = d.x; c.d[1] = d.y; c.d[2] = d.z; c.d[3] = d.w;
     }
     return c;
@@ -107,27 +114,27 @@ __device__ __forceinline__ LaneCodes<FMT> load_codes_buf(Rsrc r, uint32_t lane)
 // Raw scale bits of the lane's blocks: one scale (32-element blocks), two
 // adjacent scales (16), or the pair's shared scale (64), read at the
 // scale region's offset.
-template <int FMT, int SC, int BL>
+template <int FMT, int SC, int BL, int AUX = kNT>
 __device__ __forceinline__ void load_scale_bits(Rsrc r, uint32_t lane, uint32_t (&bits)[Halves<BL>::v])
 {
     constexpr uint32_t base = Fmt<FMT>::code_bytes;
     constexpr uint32_t SB = ScaleBytes<SC>::v;
     if constexpr (BL == 16) {
         if constexpr (SB == 2) {
-            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, base + lane * 4u, 0, kNT);
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, base + lane * 4u, 0, AUX);
             bits[0] = w & 0xFFFFu; bits[1] = w >> 16;
         } else if constexpr (SB == 4) {
-            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, base + lane * 8u, 0, kNT);
+            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, base + lane * 8u, 0, AUX);
             bits[0] = w.x; bits[1] = w.y;
         } else {
-            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b16(r, base + lane * 2u, 0, kNT);
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b16(r, base + lane * 2u, 0, AUX);
             bits[0] = w & 0xFFu; bits[1] = w >> 8;
         }
     } else {
         const uint32_t idx = (BL == 64) ? (lane >> 1) : lane;
-        if constexpr (SB == 2) bits[0] = __builtin_amdgcn_raw_buffer_load_b16(r, base + idx * 2u, 0, kNT);
-        else if constexpr (SB == 4) bits[0] = __builtin_amdgcn_raw_buffer_load_b32(r, base + idx * 4u, 0, kNT);
-        else bits[0] = __builtin_amdgcn_raw_buffer_load_b8(r, base + idx, 0, kNT);
+        if constexpr (SB == 2) bits[0] = __builtin_amdgcn_raw_buffer_load_b16(r, base + idx * 2u, 0, AUX);
+        else if constexpr (SB == 4) bits[0] = __builtin_amdgcn_raw_buffer_load_b32(r, base + idx * 4u, 0, AUX);
+        else bits[0] = __builtin_amdgcn_raw_buffer_load_b8(r, base + idx, 0, AUX);
     }
 }
 
@@ -138,12 +145,12 @@ struct LaneBlock {
     uint32_t sbits[Halves<BL>::v];
 };
 
-template <int FMT, int SC, int BL>
+template <int FMT, int SC, int BL, int AUX = kNT>
 __device__ __forceinline__ LaneBlock<FMT, SC, BL> load_lane_block(Rsrc r, uint32_t lane)
 {
     LaneBlock<FMT, SC, BL> b;
-    b.c = load_codes_buf<FMT>(r, lane);
-    load_scale_bits<FMT, SC, BL>(r, lane, b.sbits);
+    b.c = load_codes_buf<FMT, AUX>(r, lane);
+    load_scale_bits<FMT, SC, BL, AUX>(r, lane, b.sbits);
     return b;
 }
 
@@ -516,9 +523,10 @@ __device__ __forceinline__ void store_block_guarded(void* __restrict__ out, size
 }
 
 // One wave unpacks one tile per iteration: codes in through per-lane buffer
-// loads, decoded values out either through a padded LDS row per lane and
-// wave-coalesced 16-byte stores (RC_UNPACK_LDS) or straight from each lane.
-template <int FMT, int SC, int BL, int ODT>
+// loads (cache policy LDA), decoded values out either through a padded LDS
+// row per lane and wave-coalesced 16-byte stores (RC_UNPACK_LDS) or straight
+// from each lane.
+template <int FMT, int SC, int BL, int ODT, int LDA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ODT == kF32 ? 4 : 8)))
 void unpack_kernel(const uint8_t* __restrict__ in, size_t n, void* __restrict__ out, size_t tiles)
 {
@@ -536,7 +544,7 @@ void unpack_kernel(const uint8_t* __restrict__ in, size_t n, void* __restrict__ 
 #endif
     for (size_t tile = tw.first; tile < full; tile += tw.stride) {
         float d[32];
-        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL>(span_rsrc(in, tile * TB, TB), lane), d);
+        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL, LDA>(span_rsrc(in, tile * TB, TB), lane), d);
         uint32_t wd[32];
         out_words<ODT>(d, wd);
         const Rsrc dst = span_rsrc(out, tile * (size_t)(kTile * ES), kTile * ES);
@@ -562,7 +570,7 @@ void unpack_kernel(const uint8_t* __restrict__ in, size_t n, void* __restrict__ 
     }
     if (full != tiles && full % tw.stride == tw.first) {     // the partial last tile
         float d[32];
-        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL>(span_rsrc(in, full * TB, TB), lane), d);
+        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL, LDA>(span_rsrc(in, full * TB, TB), lane), d);
         store_block_guarded<ODT>(out, full * kTile + (size_t)lane * 32, n, d);
     }
 }
@@ -820,11 +828,22 @@ hipError_t launch_unpack_t(const void* in, size_t n, int dt, void* out, hipStrea
 {
     const size_t tiles = (n + kTile - 1) / kTile;
     const uint8_t* i = static_cast<const uint8_t*>(in);
-    switch (dt) {
-    case kF32: hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kF32>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break;
-    case kF16: hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kF16>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break;
-    default:   hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kBF16>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break;
+#define RC_UNPACK(LDA)                                                                                                   \
+    switch (dt) {                                                                                                        \
+    case kF32: hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kF32, LDA>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break; \
+    case kF16: hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kF16, LDA>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break; \
+    default:   hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kBF16, LDA>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break; \
     }
+    if constexpr (FMT == kFp8 || FMT == kBf8) {
+        RC_UNPACK(kNT)
+    } else {
+        if (tiles >= kUnpackPlainLoadTiles) {
+            RC_UNPACK(kPlainLoad)
+        } else {
+            RC_UNPACK(kNT)
+        }
+    }
+#undef RC_UNPACK
     return hipGetLastError();
 }
 

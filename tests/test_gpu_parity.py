@@ -404,6 +404,44 @@ def test_variant_unpack_bit_exact(name, odt):
     assert_same(g, ref, name)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", [v for v in VARIANTS if not v.startswith(("e4m3", "e5m2"))])
+def test_unpack_around_65536_tiles(name):
+    """unpack_dequant of the 3- and 4-bit codecs reads its packed tiles with
+    another cache policy from 65,536 tiles on: streams of 65,535 (ragged),
+    65,536 and 65,537 (ragged) tiles into every output dtype, checked on
+    sampled tiles.  The packed stream is the oracle's: picked tiles hold the
+    oracle's codes of mixed values, every other tile is zero bytes."""
+    c, oc = rca.ALL_CODECS[name], oracle.ALL_CODECS[name]
+    tb = oracle.tile_bytes(oc)
+    pool = mixed(61 * 2048, seed=len(name) * 7 + 3, dt="fp32")
+    rng = np.random.default_rng(len(name))
+    for n in (65535 * 2048 - 1000, 65536 * 2048, 65536 * 2048 + 777):
+        tiles = -(-n // 2048)
+        say(f"case unpack around 65536 tiles {name} n={n} tiles={tiles}")
+        picks = sample_tiles(tiles, rng)
+        packed = np.zeros(oracle.packed_bytes(oc, n), dtype=np.uint8)
+        ref_tiles = {}
+        for t in picks:
+            cnt = min(2048, n - t * 2048)
+            src = pool[(t % 61) * 2048:(t % 61) * 2048 + cnt]
+            ref_tiles[t] = (oracle.quantize_pack(oc, src, dtype=oracle.DT_FP32), cnt)
+            packed[t * tb:(t + 1) * tb] = ref_tiles[t][0]
+        dev_packed = torch.from_numpy(packed).to(DEV)
+        for odt in DTYPES:
+            y = rca.unpack_dequant(dev_packed, c, n, TORCH_DT[odt])
+            assert y.numel() == n
+            for t in picks:
+                ref_p, cnt = ref_tiles[t]
+                ref = oracle.unpack_dequant(oc, ref_p, cnt, ORACLE_DT[odt])
+                g = y[t * 2048:t * 2048 + cnt].cpu()
+                g = g.numpy() if odt == "fp32" else g.view(torch.int16).numpy().view(np.uint16)
+                assert_same(g, ref, f"{name} n={n} odt={odt} tile {t}")
+            del y
+        del dev_packed
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", VARIANTS)
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 8])
 def test_variant_reduce_bit_exact(name, k):
