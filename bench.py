@@ -400,15 +400,23 @@ def table(args):
                              (lambda K: lambda i: rca.dequant_reduce_requant(bufs[i % sets][1][:K], codec, n,
                                                                               out=bufs[i % sets][2]))(K),
                              (K + 1) * pb, K * 2 * n))
+            # unpack reads nothing but a packed stream: it walks over all the
+            # packed streams of the sets, cloned up to 1 GiB, so that the
+            # streams one graph reads (30 launches) exceed the 256 MiB
+            # Infinity Cache (its plain loads of large streams would hit there)
+            packs = [st for b in bufs for st in b[1]]
+            while len(packs) * pb < (1 << 30) and len(packs) < 30:
+                packs.append(packs[len(packs) % (sets * kmax)].clone())
+            npk = len(packs)
             rows.append(("unpack_dequant bf16",
-                         lambda i: rca.unpack_dequant(bufs[i % sets][2], codec, n, torch.bfloat16, out=bufs[i % sets][3]),
+                         lambda i: rca.unpack_dequant(packs[i % npk], codec, n, torch.bfloat16, out=bufs[i % sets][3]),
                          pb + 2 * n, 2 * n))
             for name, fn, hbm, unc in rows:
                 ms = timed(fn)
                 g = hbm / (ms * 1e-3) / 1e9
                 print(f"| {mib} | {fmt} | {name} | {ms * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
                       f"{unc / (ms * 1e-3) / 1e9:.0f} |", flush=True)
-            del bufs
+            del bufs, packs
             torch.cuda.empty_cache()
     return 0
 
