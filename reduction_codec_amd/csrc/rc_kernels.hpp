@@ -4,11 +4,11 @@
 // launcher declarations of rc_launch.hpp.
 //
 // One wave64 per 2048-element tile, lane l = elements 32l..32l+31;
-// 256-thread workgroups (four waves).  Packed tiles are read and written with
-// per-lane buffer accesses that are contiguous across the wave (code words at
-// lane * bytes per 32 elements, FP8 codes as two 16-byte planes, scales at
-// lane * scale bytes per lane); the
-// 64- or 128-byte element rows of quantize input and unpack output are
+// 256-thread workgroups (four waves), one-wave ones for the INT reduce.
+// Packed tiles are read and written with per-lane buffer accesses that are
+// contiguous across the wave (code words at lane * bytes per 32 elements,
+// FP8 codes as two 16-byte planes, scales at lane * scale bytes per lane);
+// the 64- or 128-byte element rows of quantize input and unpack output are
 // regrouped through LDS so that HBM sees wave-coalesced 16-byte chunks.
 #pragma once
 
@@ -16,7 +16,7 @@
 #include "rc_launch.hpp"
 
 #ifndef RC_GROUPS_PER_CU
-#define RC_GROUPS_PER_CU 256                       // grid cap, workgroups per CU
+#define RC_GROUPS_PER_CU 256                       // grid cap, four-wave workgroups per CU
 #endif
 #ifndef RC_REDUCE_WAVES
 #define RC_REDUCE_WAVES 8                          // reduce occupancy target (waves per SIMD), INT / MX
@@ -797,10 +797,10 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------- launchers ----
 
-// Grid of four-wave workgroups: one tile per wave up to RC_GROUPS_PER_CU
-// workgroups per compute unit (1 GiB of bf16 input on 256 CUs; measured
-// faster there than a 4x smaller grid walking 4 tiles per wave); beyond that
-// each wave walks several tiles.
+// Grid of `waves`-wave workgroups (four, or one for the INT reduce): one
+// tile per wave up to 4 * RC_GROUPS_PER_CU waves per compute unit (1 GiB of
+// bf16 input on 256 CUs; measured faster there than a 4x smaller grid
+// walking 4 tiles per wave); beyond that each wave walks several tiles.
 static inline dim3 tile_grid(size_t tiles, int waves = kWavesPerGroup)
 {
     int dev = 0, cus = 256;

@@ -74,3 +74,17 @@ def test_summarize_trace_table(tmp_path, capsys):
     assert out[0].startswith("| kernel | calls | avg ns")
     assert out[2] == "| void rc::reduce_kernel<2, 1, 32, 4> | 2 | 15500 | 15000 | 16000 | 31000 |"
     assert out[3] == "| rc::copy_kernel | 1 | 1000 | 1000 | 1000 | 1000 |"
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "k.hpp"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", ["k.hpp"])
+    src.write_text('// header\nint f(int x) { return x + 1; }  /* note */\nconst char* s = "a // b";\n')
+    h0 = bench.kernel_source_hash()
+    src.write_text('// another header\n\nint f(int x)  { return x + 1; }\n/* longer\n note */ const char* s = "a // b";\n')
+    assert bench.kernel_source_hash() == h0                      # comments and layout only
+    src.write_text('// header\nint f(int x) { return x + 2; }  /* note */\nconst char* s = "a // b";\n')
+    assert bench.kernel_source_hash() != h0                      # code
+    src.write_text('// header\nint f(int x) { return x + 1; }  /* note */\nconst char* s = "a /// b";\n')
+    assert bench.kernel_source_hash() != h0                      # a string literal is code
