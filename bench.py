@@ -317,22 +317,30 @@ def main():
     unc = 2 * n + K * 2 * n                   # uncompressed bytes processed per step
     value = unc / (ms * 1e-3) / 1e9
     step_hbm = (q_bytes + r_bytes) / (ms * 1e-3) / 1e9
-    dom_key, dom_bytes, dom_ms = ("reduce_kernel", r_bytes, r_ms) if r_ms >= q_ms else \
-        ("quantize_kernel", q_bytes, q_ms)
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(dom_key),
-            "kernel": f"{dom_key}<{args.fmt}" + (f", K={K}>" if dom_key == "reduce_kernel" else ", bf16>"),
-            "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)}
-    valu = counters_for(dom_key).get("valu_insts")
-    if valu:
-        # the same launch against the vector-ALU issue limit: wave64 VALU
-        # instructions (SQ_INSTS_VALU) per launch / launch time, against one
-        # instruction per 4 cycles on each of 256 x 4 SIMDs at 2.4 GHz
-        rate = valu / (dom_ms * 1e-3) / 1e9
-        roof["alu"] = {"valu_insts_per_launch": int(valu), "achieved": round(rate, 1),
-                       "peak": VALU_PEAK_GINST, "unit": "G wave64 VALU instructions/s",
-                       "frac": round(rate / VALU_PEAK_GINST, 4)}
+    def kernel_roof(key, nbytes, kms):
+        achieved = nbytes / (kms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(key),
+             "kernel": f"{key}<{args.fmt}" + (f", K={K}>" if key == "reduce_kernel" else ", bf16>"),
+             "bytes_per_launch": nbytes, "avg_launch_ms": round(kms, 5)}
+        valu = counters_for(key).get("valu_insts")
+        if valu:
+            # the same launch against the vector-ALU issue limit: wave64 VALU
+            # instructions (SQ_INSTS_VALU) per launch / launch time, against one
+            # instruction per 4 cycles on each of 256 x 4 SIMDs at 2.4 GHz
+            rate = valu / (kms * 1e-3) / 1e9
+            r["alu"] = {"valu_insts_per_launch": int(valu), "achieved": round(rate, 1),
+                        "peak": VALU_PEAK_GINST, "unit": "G wave64 VALU instructions/s",
+                        "frac": round(rate / VALU_PEAK_GINST, 4)}
+        return r
+
+    # the dominant kernel is the longer of the two launches; both are listed,
+    # since at some sizes they take about the same time
+    per_kernel = {"quantize_kernel": kernel_roof("quantize_kernel", q_bytes, q_ms),
+                  "reduce_kernel": kernel_roof("reduce_kernel", r_bytes, r_ms)}
+    dom_key = "reduce_kernel" if r_ms >= q_ms else "quantize_kernel"
+    roof = dict(per_kernel[dom_key])
+    roof["per_kernel"] = per_kernel
 
     cpu = None
     if not args.no_cpu:
