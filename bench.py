@@ -414,6 +414,12 @@ def table(args):
         g = 4 * n / (ms * 1e-3) / 1e9
         print(f"| {mib} | - | copy bf16 (reference) | {ms * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
               f"{2 * n / (ms * 1e-3) / 1e9:.0f} |", flush=True)
+        # and a write-only reference for the write-heavy unpack: torch's fill of
+        # the same bf16 bytes
+        ms = timed(lambda i: cbufs[i % csets][1].fill_(1.0))
+        g = 2 * n / (ms * 1e-3) / 1e9
+        print(f"| {mib} | - | fill bf16, write only (reference) | {ms * 1e3:.2f} | {g:.0f} | "
+              f"{100 * g / HBM_PEAK_GBS:.1f} | - |", flush=True)
         del cbufs
         for fmt in names:
             codec = rca.CODECS[fmt] if fmt in rca.CODECS else rca.ALL_CODECS[fmt]
