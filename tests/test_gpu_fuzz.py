@@ -6,8 +6,11 @@ Hypothesis draws the codec (any of the 33), the input dtype, the length
 is an fp16 subnormal or flushes to zero, fp32 denormals, saturating and huge
 blocks, outliers); every example quantizes K streams, reduces them with the
 FP32 sums and unpacks the result, each step compared byte for byte with the
-oracle.  The example sequence is derandomized, so a run is reproducible.
+oracle.  By default the 120-example sequence is derandomized, so a run is
+reproducible; RC_FUZZ_EXAMPLES=N runs N examples with fresh random draws.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -23,6 +26,7 @@ DEV = torch.device("cuda:0")
 DTYPES = {"bf16": (torch.bfloat16, oracle.DT_BF16), "fp16": (torch.float16, oracle.DT_FP16),
           "fp32": (torch.float32, oracle.DT_FP32)}
 CODECS = sorted(rca.ALL_CODECS)
+EXAMPLES = int(os.environ.get("RC_FUZZ_EXAMPLES", "120"))
 
 
 def make_values(rng: np.random.Generator, n: int, kinds, k: int, dt: str) -> np.ndarray:
@@ -60,7 +64,7 @@ def to_dev(x: np.ndarray, dt: str) -> torch.Tensor:
     return (t.view(DTYPES[dt][0]) if dt != "fp32" else t).to(DEV)
 
 
-@settings(max_examples=120, deadline=None, derandomize=True, database=None,
+@settings(max_examples=EXAMPLES, deadline=None, derandomize=EXAMPLES == 120, database=None,
           suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 @given(name=st.sampled_from(CODECS), dt=st.sampled_from(sorted(DTYPES)),
        n=st.integers(min_value=1, max_value=3 * 2048 + 200), k=st.integers(min_value=1, max_value=6),
