@@ -6,7 +6,10 @@ blocks whose fp16 scale is subnormal or flushes, fp32 denormals, saturating
 and huge blocks, outliers).  The oracle's packed bytes must equal
 tests/brute.py's (exact rationals: argmin over every code), its decode must
 equal brute force decode, and a 2-stream reduce must equal brute force.
-Derandomized: the same examples every run."""
+Derandomized by default (the same 30 examples every run); RC_FUZZ_EXAMPLES=N
+runs N examples with fresh random draws."""
+import os
+
 import numpy as np
 from hypothesis import HealthCheck, given, settings
 from hypothesis import strategies as st
@@ -15,6 +18,7 @@ import oracle
 from tests import brute
 
 CODECS = sorted(oracle.ALL_CODECS)
+EXAMPLES = int(os.environ.get("RC_FUZZ_EXAMPLES", "30"))
 
 
 def values(rng: np.random.Generator, n: int, kinds) -> np.ndarray:
@@ -44,7 +48,7 @@ def values(rng: np.random.Generator, n: int, kinds) -> np.ndarray:
     return v
 
 
-@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+@settings(max_examples=EXAMPLES, deadline=None, derandomize=EXAMPLES == 30, database=None,
           suppress_health_check=[HealthCheck.too_slow])
 @given(name=st.sampled_from(CODECS), n=st.integers(min_value=1, max_value=2048 + 300),
        seed=st.integers(min_value=0, max_value=2**31 - 1),
