@@ -112,10 +112,24 @@ def _codec(c) -> Codec:
     return Codec(*c)
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, dev: torch.device) -> ctypes.c_void_p:
+    """The HIP stream to launch on: the given one (which must belong to the
+    tensors' device) or that device's current stream."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _same_device(dev: torch.device, *named):
+    for name, t in named:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
 
 def _mine(t: torch.Tensor, stream) -> torch.Tensor:
@@ -152,16 +166,19 @@ def quantize_pack(x: torch.Tensor, codec, out: torch.Tensor | None = None, strea
     flat) into ``packed_bytes(codec, x.numel())`` bytes."""
     c = _codec(codec)
     _check_dev(x, "x")
+    hs = _stream(stream, x.device)
     if x.dtype not in _DTYPES:
         raise ValueError(f"unsupported input dtype {x.dtype}")
     n = x.numel()
     if out is None:
         out = _mine(torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=x.device), stream)
     _check_dev(out, "out")
+    _same_device(x.device, ("out", out))
     if out.numel() < packed_bytes(c, n) or out.dtype != torch.uint8:
         raise ValueError("out must be a uint8 tensor of packed_bytes(codec, n) bytes")
-    _ok(lib().rc_quantize_pack(c, _DTYPES[x.dtype], x.data_ptr(), n, out.data_ptr(), _stream(stream)),
-        "rc_quantize_pack")
+    with torch.cuda.device(x.device):
+        _ok(lib().rc_quantize_pack(c, _DTYPES[x.dtype], x.data_ptr(), n, out.data_ptr(), hs),
+            "rc_quantize_pack")
     return out
 
 
@@ -170,17 +187,20 @@ def unpack_dequant(packed: torch.Tensor, codec, n: int, dtype: torch.dtype = tor
     """Decode the first n elements of a packed stream to dtype."""
     c = _codec(codec)
     _check_dev(packed, "packed")
-    if packed.numel() < packed_bytes(c, n):
+    hs = _stream(stream, packed.device)
+    if _nbytes(packed) < packed_bytes(c, n):
         raise ValueError("packed is shorter than packed_bytes(codec, n)")
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported output dtype {dtype}")
     if out is None:
         out = _mine(torch.empty(n, dtype=dtype, device=packed.device), stream)
     _check_dev(out, "out")
+    _same_device(packed.device, ("out", out))
     if out.numel() < n or out.dtype != dtype:
         raise ValueError("out must hold n elements of dtype")
-    _ok(lib().rc_unpack_dequant(c, packed.data_ptr(), n, _DTYPES[dtype], out.data_ptr(), _stream(stream)),
-        "rc_unpack_dequant")
+    with torch.cuda.device(packed.device):
+        _ok(lib().rc_unpack_dequant(c, packed.data_ptr(), n, _DTYPES[dtype], out.data_ptr(), hs),
+            "rc_unpack_dequant")
     return out
 
 
@@ -194,26 +214,33 @@ def dequant_reduce_requant(streams, codec, n: int, out: torch.Tensor | None = No
     if not 1 <= k <= MAX_STREAMS:
         raise ValueError(f"need 1..{MAX_STREAMS} streams, got {k}")
     need = packed_bytes(c, n)
+    dev = streams[0].device if streams and isinstance(streams[0], torch.Tensor) else None
     for j, s in enumerate(streams):
         _check_dev(s, f"streams[{j}]")
-        if s.numel() < need:
+        _same_device(dev, (f"streams[{j}]", s))
+        if _nbytes(s) < need:
             raise ValueError(f"streams[{j}] is shorter than packed_bytes(codec, n)")
-    dev = streams[0].device
+    hs = _stream(stream, dev)
     if out is None:
         out = _mine(torch.empty(need, dtype=torch.uint8, device=dev), stream)
     _check_dev(out, "out")
+    _same_device(dev, ("out", out))
+    if _nbytes(out) < need:
+        raise ValueError("out is shorter than packed_bytes(codec, n)")
     sums = None
     if isinstance(sum_out, torch.Tensor):
         sums = sum_out
         _check_dev(sums, "sum_out")
+        _same_device(dev, ("sum_out", sums))
         if sums.dtype != torch.float32 or sums.numel() < n:
             raise ValueError("sum_out must hold n float32 values")
     elif sum_out:
         sums = _mine(torch.empty(n, dtype=torch.float32, device=dev), stream)
     ptrs = (ctypes.c_void_p * k)(*[s.data_ptr() for s in streams])
-    _ok(lib().rc_dequant_reduce_requant(c, ptrs, k, n, out.data_ptr(),
-                                        sums.data_ptr() if sums is not None else None, _stream(stream)),
-        "rc_dequant_reduce_requant")
+    with torch.cuda.device(dev):
+        _ok(lib().rc_dequant_reduce_requant(c, ptrs, k, n, out.data_ptr(),
+                                            sums.data_ptr() if sums is not None else None, hs),
+            "rc_dequant_reduce_requant")
     return out, sums
 
 
@@ -231,27 +258,33 @@ def allreduce_emulate(msgs, codec, two_shot: bool = True, out: torch.Tensor | No
     if dt not in _DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
     n = msgs[0].numel()
+    dev = msgs[0].device
     for j, m in enumerate(msgs):
         _check_dev(m, f"msgs[{j}]")
+        _same_device(dev, (f"msgs[{j}]", m))
         if m.dtype != dt or m.numel() != n:
             raise ValueError("all messages need the same dtype and length")
+    hs = _stream(stream, dev)
     if out is None:
-        out = _mine(torch.empty(n, dtype=dt, device=msgs[0].device), stream)
+        out = _mine(torch.empty(n, dtype=dt, device=dev), stream)
     _check_dev(out, "out")
+    _same_device(dev, ("out", out))
     if out.dtype != dt or out.numel() < n:
         raise ValueError("out must hold n elements of the messages' dtype")
     packed = None
     if isinstance(packed_out, torch.Tensor):
         packed = packed_out
         _check_dev(packed, "packed_out")
+        _same_device(dev, ("packed_out", packed))
         if packed.numel() < packed_bytes(c, n) or packed.dtype != torch.uint8:
             raise ValueError("packed_out must be a uint8 tensor of packed_bytes(codec, n) bytes")
     elif packed_out:
-        packed = _mine(torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=msgs[0].device), stream)
+        packed = _mine(torch.empty(packed_bytes(c, n), dtype=torch.uint8, device=dev), stream)
     ptrs = (ctypes.c_void_p * k)(*[m.data_ptr() for m in msgs])
-    _ok(lib().rc_allreduce_emulate(c, _DTYPES[dt], ptrs, k, n, 1 if two_shot else 0, out.data_ptr(),
-                                   packed.data_ptr() if packed is not None else None, _stream(stream)),
-        "rc_allreduce_emulate")
+    with torch.cuda.device(dev):
+        _ok(lib().rc_allreduce_emulate(c, _DTYPES[dt], ptrs, k, n, 1 if two_shot else 0, out.data_ptr(),
+                                       packed.data_ptr() if packed is not None else None, hs),
+            "rc_allreduce_emulate")
     return out, packed
 
 
@@ -261,6 +294,8 @@ def mxfp4_gemv(w_packed: torch.Tensor, rows: int, cols: int, x: torch.Tensor, ou
     MXFP4 codec; cols a multiple of 2048.  See rc_mxfp4_gemv."""
     _check_dev(w_packed, "w_packed")
     _check_dev(x, "x")
+    _same_device(w_packed.device, ("x", x))
+    hs = _stream(stream, w_packed.device)
     if w_packed.dtype != torch.uint8 or w_packed.numel() < packed_bytes(MXFP4, rows * cols):
         raise ValueError("w_packed must hold packed_bytes(MXFP4, rows * cols) bytes")
     if x.dtype not in _DTYPES or x.numel() < cols:
@@ -270,10 +305,12 @@ def mxfp4_gemv(w_packed: torch.Tensor, rows: int, cols: int, x: torch.Tensor, ou
     if out is None:
         out = _mine(torch.empty(rows, dtype=out_dtype, device=x.device), stream)
     _check_dev(out, "out")
+    _same_device(w_packed.device, ("out", out))
     if out.dtype != out_dtype or out.numel() < rows:
         raise ValueError("out must hold rows values of out_dtype")
-    _ok(lib().rc_mxfp4_gemv(w_packed.data_ptr(), rows, cols, _DTYPES[x.dtype], x.data_ptr(), _DTYPES[out_dtype],
-                            out.data_ptr(), _stream(stream)), "rc_mxfp4_gemv")
+    with torch.cuda.device(w_packed.device):
+        _ok(lib().rc_mxfp4_gemv(w_packed.data_ptr(), rows, cols, _DTYPES[x.dtype], x.data_ptr(), _DTYPES[out_dtype],
+                                out.data_ptr(), hs), "rc_mxfp4_gemv")
     return out
 
 
@@ -281,8 +318,11 @@ def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> torch.Tensor:
     """Byte copy through the library's 16-byte vector copy kernel."""
     _check_dev(dst, "dst")
     _check_dev(src, "src")
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < nbytes:
+    _same_device(src.device, ("dst", dst))
+    hs = _stream(stream, src.device)
+    nbytes = _nbytes(src)
+    if _nbytes(dst) < nbytes:
         raise ValueError("dst too small")
-    _ok(lib().rc_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)), "rc_copy")
+    with torch.cuda.device(src.device):
+        _ok(lib().rc_copy(src.data_ptr(), dst.data_ptr(), nbytes, hs), "rc_copy")
     return dst

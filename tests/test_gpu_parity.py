@@ -247,6 +247,46 @@ def test_zero_length_and_errors_on_gpu():
         rca.dequant_reduce_requant([out], rca.Codec(2, 2, 32), 0)
 
 
+def test_binding_rejects_short_buffers_before_launching():
+    """Buffers smaller than the call needs are refused by the binding with
+    ValueError, before anything runs; the buffers keep their contents."""
+    n = 2 * 2048 + 5
+    x = torch.ones(n, dtype=torch.bfloat16, device=DEV)
+    pb = rca.packed_bytes(rca.INT3, n)
+    p = rca.quantize_pack(x, rca.INT3)
+    short = torch.full((pb - 1,), 0x5A, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        rca.quantize_pack(x, rca.INT3, out=short)
+    with pytest.raises(ValueError):
+        rca.dequant_reduce_requant([p, p], rca.INT3, n, out=short)
+    with pytest.raises(ValueError):
+        rca.dequant_reduce_requant([p, short], rca.INT3, n)
+    with pytest.raises(ValueError):
+        rca.dequant_reduce_requant([p], rca.INT3, n, sum_out=torch.empty(n - 1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        rca.unpack_dequant(short, rca.INT3, n)
+    with pytest.raises(ValueError):
+        rca.unpack_dequant(p, rca.INT3, n, out=torch.empty(n - 1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        rca.allreduce_emulate([x, x[:-1]], rca.INT3)
+    with pytest.raises(ValueError):
+        rca.copy(short[:16], p[:32])
+    torch.cuda.synchronize()
+    assert bool((short == 0x5A).all())
+    # a packed stream may be any dtype; its bytes are what count
+    out, _ = rca.dequant_reduce_requant([p.view(torch.int32)[: pb // 4]], rca.INT3, n)
+    assert torch.equal(out, rca.dequant_reduce_requant([p], rca.INT3, n)[0])
+
+
+def test_binding_rejects_a_stream_of_another_device():
+    class OtherDeviceStream:
+        device = torch.device("cuda", 1)
+        cuda_stream = 0
+    x = torch.ones(2048, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        rca.quantize_pack(x, rca.INT3, stream=OtherDeviceStream())
+
+
 # -------------------------------------------------------- configurations ----
 
 def test_config_int4_fp16_64_tiles_roundtrip_and_k2():
