@@ -289,7 +289,7 @@ __device__ __forceinline__ EncScale enc_scale(float a)
     if constexpr (FMT == 1 || FMT == 2) {
         if constexpr (SC == kS16) {
             const IntScale sc = int_scale<Fmt<FMT>::qmax>(a);
-            r.bits = sc.zero ? 0u : sc.bits;
+            r.bits = sc.bits;                            // +0 for a zero block (a >= 0)
             r.m = sc.r;
             r.zero = sc.zero;
             r.clamp = sc.abnormal;
@@ -417,11 +417,14 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
 #pragma unroll
         for (int g = 0; g < 4; ++g) N[g] = int3_clamp_word(N[g]);
     }
+    // A zero block (FP16 scale 0) has multiplier 0, so its magnitudes are
+    // already 0; only the signs of its negative elements (x * 0 = -0) remain,
+    // and they all sit in the sign plane: elements 0-15 in bits 0-15.
     uint32_t keep = sc[0].zero ? 0u : 0xFFFFFFFFu;
     if constexpr (H == 2) keep = (sc[0].zero ? 0u : 0x0000FFFFu) | (sc[1].zero ? 0u : 0xFFFF0000u);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) N[g] &= keep;
-    return int3_planes(N);
+    Int3Words o = int3_planes(N);
+    o.h &= keep;
+    return o;
 }
 
 // acc[e] (+)= q_e * S for the 32 elements: E2M1 decode of the nibble (q/2)
