@@ -613,6 +613,18 @@ def cpu_baseline(args, host, n, K):
         if dt >= 1.5 or reps >= 50:
             break
     unc = reps * (2 * ns + K * 2 * ns)
+    # and one thread on a smaller sample of the same message (about 1.5 s)
+    ns1 = min(ns, 1024 * 2048)
+    peers1 = [p[:oracle.packed_bytes(c, ns1)] for p in peers]
+    reps1, t1 = 0, time.perf_counter()
+    while True:
+        p0 = oracle.quantize_pack_parallel(c, msgs[0][:ns1], dtype=oracle.DT_BF16, threads=1)
+        oracle.dequant_reduce_requant_parallel(c, [p0] + peers1[1:], ns1, threads=1)
+        reps1 += 1
+        dt1 = time.perf_counter() - t1
+        if dt1 >= 1.5 or reps1 >= 50:
+            break
+    unc1 = reps1 * (2 * ns1 + K * 2 * ns1)
     model = ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -621,7 +633,9 @@ def cpu_baseline(args, host, n, K):
         pass
     return {"value": round(unc / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": model,
             "sample": f"{sample_tiles} tiles ({ns} elements) of the same message and peers, {reps} repetitions of "
-                      f"quantize + {K}-stream reduce, tile ranges over {threads} threads, {dt:.2f} s wall"}
+                      f"quantize + {K}-stream reduce, tile ranges over {threads} threads, {dt:.2f} s wall",
+            "single_thread": {"value": round(unc1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"the first {ns1 // 2048} tiles, {reps1} repetitions, {dt1:.2f} s wall"}}
 
 
 if __name__ == "__main__":
