@@ -372,7 +372,8 @@ void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict_
 // j - 2 is decoded; the same two streams in flight as batches of two, but
 // each load issued earlier): 1.4-4.9 % faster at 64 MiB, neutral from
 // 256 MiB.  Not for INT with E8M0 scales, whose decode holds more registers
-// (there it spilled: 8-11 % slower), nor FP8 (batches of four).
+// (there it spilled: 8-11 % slower), nor FP8 (batches of four; rolling
+// four deep measured within +-1 %).
 template <int FMT, int SC> struct ReduceRoll {
     static constexpr bool v = RC_REDUCE_ROLL && FMT != kFp8 && FMT != kBf8 &&
                               !((FMT == kInt3 || FMT == kInt4) && SC == kSE8);
