@@ -39,6 +39,12 @@
 #ifndef RC_QUANT_WAVES
 #define RC_QUANT_WAVES 8                           // quantize occupancy target, waves per SIMD
 #endif
+#ifndef RC_QUANT_F32_HALVES
+#define RC_QUANT_F32_HALVES 1                      // fp32 quantize input regrouped in two halves
+#endif
+#ifndef RC_QUANT_F32_WAVES
+#define RC_QUANT_F32_WAVES 4                       // fp32 quantize occupancy target (5, 6: no gain)
+#endif
 #ifndef RC_QUANT_LDS
 #define RC_QUANT_LDS 1                             // quantize input regrouped through LDS
 #endif
@@ -307,11 +313,12 @@ __device__ __forceinline__ void widen_chunks(const u32x4 (&c)[CPB], float (&v)[3
 // (its exact-quotient encoder then holds its values without spilling:
 // measured 3 % faster than 8 at 64 MiB); the others at RC_QUANT_WAVES.
 template <int FMT, int DT> struct QuantWaves {
-    static constexpr int v = DT == kF32 ? 4 : ((FMT == kFp8 || FMT == kBf8) ? 7 : RC_QUANT_WAVES);
+    static constexpr int v = DT == kF32 ? RC_QUANT_F32_WAVES : ((FMT == kFp8 || FMT == kBf8) ? 7 : RC_QUANT_WAVES);
 };
 
 // One wave quantizes one whole tile per iteration (fp32 input: the padded
-// LDS rows of four waves take 36 KiB, so at most 4 waves per SIMD fit).
+// 128-byte rows pass through LDS in two halves of 32 rows, 4.5 KiB per wave;
+// measured 2-3 % faster at 64 MiB than all 64 rows at once).
 // With RC_QUANT_LDS the
 // tile's input is read as wave-coalesced 16-byte chunks (chunk c by lane
 // c % 64) and regrouped through a padded LDS row per lane; otherwise each
@@ -333,7 +340,11 @@ void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict_
     const size_t full = n / kTile;
 #if RC_QUANT_LDS
     constexpr int ROW = BB + 16;               // padded LDS row: conflict-free 16-byte reads
-    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][64 * ROW];
+    // fp32 (RC_QUANT_F32_HALVES): the rows of lanes 0-31, then of lanes
+    // 32-63, pass through one 32-row buffer (half the LDS per wave)
+    constexpr bool HALVES = RC_QUANT_F32_HALVES && DT == kF32;
+    constexpr int ROWS = HALVES ? 32 : 64;
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][ROWS * ROW];
     uint8_t* lds = sm[tw.w];
 #endif
     for (size_t tile = tw.first; tile < full; tile += tw.stride) {
@@ -343,15 +354,36 @@ void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict_
 #if RC_QUANT_LDS
 #pragma unroll
         for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (64u * i + lane) * 16u, 0, kNT);
-        wave_lds_sync();                       // the previous tile's rows are fully read
+        if constexpr (HALVES) {
+            // loads 0..CPB/2-1 hold the chunks of rows 0-31, the rest rows 32-63
+            u32x4 r[CPB];
 #pragma unroll
-        for (int i = 0; i < CPB; ++i) {
-            const uint32_t ch = 64u * i + lane;
-            *reinterpret_cast<u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16) = c[i];
+            for (int h = 0; h < 2; ++h) {
+                wave_lds_sync();               // the buffer's previous rows are fully read
+#pragma unroll
+                for (int i = 0; i < CPB / 2; ++i) {
+                    const uint32_t ch = 64u * i + lane;              // chunk within the half
+                    *reinterpret_cast<u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16) = c[h * (CPB / 2) + i];
+                }
+                wave_lds_sync();
+                if ((lane >> 5) == (uint32_t)h) {
+#pragma unroll
+                    for (int i = 0; i < CPB; ++i) r[i] = *reinterpret_cast<const u32x4*>(lds + (lane & 31u) * ROW + 16 * i);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) c[i] = r[i];
+        } else {
+            wave_lds_sync();                   // the previous tile's rows are fully read
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) {
+                const uint32_t ch = 64u * i + lane;
+                *reinterpret_cast<u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16) = c[i];
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) c[i] = *reinterpret_cast<const u32x4*>(lds + lane * ROW + 16 * i);
         }
-        wave_lds_sync();
-#pragma unroll
-        for (int i = 0; i < CPB; ++i) c[i] = *reinterpret_cast<const u32x4*>(lds + lane * ROW + 16 * i);
 #else
 #pragma unroll
         for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, lane * BB + 16u * i, 0, kNT);
