@@ -99,6 +99,8 @@ def parse_args():
     ap.add_argument("--table-codecs", default="int3,int4,fp8,mxfp4",
                     help="comma list of codec names (default names or <elem>_<scale>_b<block>), or 'all'")
     ap.add_argument("--table-k", default="2,4,8", help="stream counts of the reduce rows")
+    ap.add_argument("--table-dt", default="bf16", choices=["bf16", "fp16", "fp32"],
+                    help="message dtype of the table: quantize input, unpack output, copy and fill")
     ap.add_argument("--gemv", action="store_true",
                     help="MXFP4 GEMV on the 4096x4096 weight recipe (no JSON line)")
     ap.add_argument("--fused", action="store_true",
@@ -372,9 +374,9 @@ def main():
 
 def table(args):
     """Average launch time of every kernel family per format and message size
-    (bf16 messages; K packed streams for the reduce), from a HIP graph of 30
-    back-to-back launches, with algorithmic HBM bytes per launch / time
-    against the 8 TB/s peak."""
+    (messages of --table-dt, bf16 by default; K packed streams for the
+    reduce), from a HIP graph of 30 back-to-back launches, with algorithmic
+    HBM bytes per launch / time against the 8 TB/s peak."""
     import numpy as np
     import torch
 
@@ -402,45 +404,48 @@ def table(args):
 
     print("| MiB | format | kernel | us | HBM GB/s | % of peak | uncompressed GB/s |")
     print("|---:|---|---|---:|---:|---:|---:|")
+    dt = args.table_dt
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dt]
+    es = 4 if dt == "fp32" else 2                   # bytes per element of the message
     for mib in [int(v) for v in args.table_mib.split(",")]:
-        n = mib * (1 << 20) // 2
-        x0 = torch.from_numpy(datagen.bf16_student4(2 * n, 0).view(np.int16)).view(torch.bfloat16).to(dev)
+        n = mib * (1 << 20) // es
+        x0 = torch.from_numpy(datagen.bf16_student4(2 * n, 0).view(np.int16)).view(torch.bfloat16).to(dev).to(tdt)
         names = sorted(rca.ALL_CODECS) if args.table_codecs == "all" else args.table_codecs.split(",")
         ks = [int(v) for v in args.table_k.split(",")]
-        # the achievable-bandwidth reference at this size: a plain copy of the bf16 message
-        csets = max(1, -(-(1 << 30) // (4 * n)))
+        # the achievable-bandwidth reference at this size: a plain copy of the message
+        csets = max(1, -(-(1 << 30) // (2 * es * n)))
         cbufs = [(x0.clone(), torch.empty_like(x0)) for _ in range(csets)]
         ms = timed(lambda i: rca.copy(cbufs[i % csets][1], cbufs[i % csets][0]))
-        g = 4 * n / (ms * 1e-3) / 1e9
-        print(f"| {mib} | - | copy bf16 (reference) | {ms * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
-              f"{2 * n / (ms * 1e-3) / 1e9:.0f} |", flush=True)
+        g = 2 * es * n / (ms * 1e-3) / 1e9
+        print(f"| {mib} | - | copy {dt} (reference) | {ms * 1e3:.2f} | {g:.0f} | {100 * g / HBM_PEAK_GBS:.1f} | "
+              f"{es * n / (ms * 1e-3) / 1e9:.0f} |", flush=True)
         # and a write-only reference for the write-heavy unpack: torch's fill of
-        # the same bf16 bytes
+        # the same bytes
         ms = timed(lambda i: cbufs[i % csets][1].fill_(1.0))
-        g = 2 * n / (ms * 1e-3) / 1e9
-        print(f"| {mib} | - | fill bf16, write only (reference) | {ms * 1e3:.2f} | {g:.0f} | "
+        g = es * n / (ms * 1e-3) / 1e9
+        print(f"| {mib} | - | fill {dt}, write only (reference) | {ms * 1e3:.2f} | {g:.0f} | "
               f"{100 * g / HBM_PEAK_GBS:.1f} | - |", flush=True)
         del cbufs
         for fmt in names:
             codec = rca.CODECS[fmt] if fmt in rca.CODECS else rca.ALL_CODECS[fmt]
             pb = rca.packed_bytes(codec, n)
             kmax = max(ks)
-            sets = max(1, -(-(1 << 30) // (4 * n + (kmax + 1) * pb)))
+            sets = max(1, -(-(1 << 30) // (2 * es * n + (kmax + 1) * pb)))
             bufs = []
             for _ in range(sets):
                 x = x0.clone()
                 p = rca.quantize_pack(x, codec)
                 streams = [p] + [p.clone() for _ in range(kmax - 1)]
                 bufs.append((x, streams, torch.empty(pb, dtype=torch.uint8, device=dev),
-                             torch.empty(n, dtype=torch.bfloat16, device=dev)))
+                             torch.empty(n, dtype=tdt, device=dev)))
             torch.cuda.synchronize()
-            rows = [("quantize_pack bf16", lambda i: rca.quantize_pack(bufs[i % sets][0], codec, out=bufs[i % sets][2]),
-                     2 * n + pb, 2 * n)]
+            rows = [(f"quantize_pack {dt}", lambda i: rca.quantize_pack(bufs[i % sets][0], codec, out=bufs[i % sets][2]),
+                     es * n + pb, es * n)]
             for K in ks:
                 rows.append((f"dequant_reduce_requant K={K}",
                              (lambda K: lambda i: rca.dequant_reduce_requant(bufs[i % sets][1][:K], codec, n,
                                                                               out=bufs[i % sets][2]))(K),
-                             (K + 1) * pb, K * 2 * n))
+                             (K + 1) * pb, K * es * n))
             # unpack reads nothing but a packed stream: it walks over all the
             # packed streams of the sets, cloned up to 1 GiB, so that the
             # streams one graph reads (30 launches) exceed the 256 MiB
@@ -449,9 +454,9 @@ def table(args):
             while len(packs) * pb < (1 << 30) and len(packs) < 30:
                 packs.append(packs[len(packs) % (sets * kmax)].clone())
             npk = len(packs)
-            rows.append(("unpack_dequant bf16",
-                         lambda i: rca.unpack_dequant(packs[i % npk], codec, n, torch.bfloat16, out=bufs[i % sets][3]),
-                         pb + 2 * n, 2 * n))
+            rows.append((f"unpack_dequant {dt}",
+                         lambda i: rca.unpack_dequant(packs[i % npk], codec, n, tdt, out=bufs[i % sets][3]),
+                         pb + es * n, es * n))
             for name, fn, hbm, unc in rows:
                 ms = timed(fn)
                 g = hbm / (ms * 1e-3) / 1e9
