@@ -83,10 +83,12 @@ constexpr int kNT = 2;                              // aux bits: nt
 // 2-4 % faster than nt alone there (and slower for the packed outputs of
 // quantize and reduce, and for the fused all-reduce's output rows).
 constexpr int kRowStore = 18;
-// Packed tiles read by unpack: with the 3- and 4-bit formats (at most
-// 0.5625 packed bytes per element, against 2-4 bytes written) plain loads
-// beat nt ones from about 128 MiB of bf16 output on (INT3 at 1 GiB: 243 ->
-// 215 us), and lose 4-6 % below 96 MiB; FP8 keeps nt loads at every size.
+// Packed tiles read by unpack: where the packed input is small next to the
+// output (the 3- and 4-bit formats, at most 0.5625 packed bytes per element
+// against 2-4 bytes written, and FP8 into fp32) plain loads beat nt ones
+// from 65,536 tiles on (INT3 to bf16 at 1 GiB: 243 -> 215 us; FP8 to fp32:
+// 5-7 %), and lose 4-6 % below 96 MiB; FP8 into bf16 or fp16 keeps nt loads
+// at every size.
 // Quantize and reduce keep nt loads (plain ones measured 2-9 % slower).
 constexpr int kPlainLoad = 0;
 constexpr size_t kUnpackPlainLoadTiles = size_t(1) << 16;
@@ -898,14 +900,11 @@ hipError_t launch_unpack_t(const void* in, size_t n, int dt, void* out, hipStrea
     case kF16: hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kF16, LDA>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break; \
     default:   hipLaunchKernelGGL((unpack_kernel<FMT, SC, BL, kBF16, LDA>), tile_grid(tiles), dim3(256), 0, st, i, n, out, tiles); break; \
     }
-    if constexpr (FMT == kFp8 || FMT == kBf8) {
-        RC_UNPACK(kNT)
+    constexpr bool F8 = FMT == kFp8 || FMT == kBf8;
+    if (tiles >= kUnpackPlainLoadTiles && (!F8 || dt == kF32)) {
+        RC_UNPACK(kPlainLoad)
     } else {
-        if (tiles >= kUnpackPlainLoadTiles) {
-            RC_UNPACK(kPlainLoad)
-        } else {
-            RC_UNPACK(kNT)
-        }
+        RC_UNPACK(kNT)
     }
 #undef RC_UNPACK
     return hipGetLastError();

@@ -445,12 +445,12 @@ def test_variant_unpack_bit_exact(name, odt):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("name", [v for v in VARIANTS if not v.startswith(("e4m3", "e5m2"))])
+@pytest.mark.parametrize("name", VARIANTS)
 def test_unpack_around_65536_tiles(name):
-    """unpack_dequant of the 3- and 4-bit codecs reads its packed tiles with
-    another cache policy from 65,536 tiles on: streams of 65,535 (ragged),
-    65,536 and 65,537 (ragged) tiles into every output dtype, checked on
-    sampled tiles.  The packed stream is the oracle's: picked tiles hold the
+    """unpack_dequant reads its packed tiles with another cache policy from
+    65,536 tiles on (3- and 4-bit codecs into any dtype, FP8 into fp32):
+    streams of 65,535 (ragged), 65,536 and 65,537 (ragged) tiles of every
+    codec into every output dtype, checked on sampled tiles.  The packed stream is the oracle's: picked tiles hold the
     oracle's codes of mixed values, every other tile is zero bytes."""
     c, oc = rca.ALL_CODECS[name], oracle.ALL_CODECS[name]
     tb = oracle.tile_bytes(oc)
