@@ -18,7 +18,9 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "librcodec_oracle.so")
+# RC_ORACLE_LIB names another build of rcodec_oracle.c (the mutation tests load
+# deliberately broken copies this way); unset, the library built beside this file.
+_LIB_PATH = os.environ.get("RC_ORACLE_LIB") or os.path.join(_HERE, "librcodec_oracle.so")
 
 TILE = 2048
 BLOCK = 32
@@ -58,7 +60,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    if not os.path.exists(_LIB_PATH) and not os.environ.get("RC_ORACLE_LIB"):
         subprocess.run(["make", "-C", _HERE], check=True, capture_output=True)
     lib = ctypes.CDLL(_LIB_PATH)
     C, vp, sz, i32 = Codec, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
