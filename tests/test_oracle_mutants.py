@@ -38,6 +38,9 @@ MUTANTS = {
     "never_rounds_up": ("if (frac > 0.5)      m = k + 1;", "if (frac > 1.5)      m = k + 1;"),
     "int_scale_over_qmax_plus_one": ("float s32 = amax / (float)qmax;",
                                      "float s32 = amax / (float)(qmax + 1);"),
+    "minifloat_ties_round_down": ("return (c % 2 == 0) ? c : c + 1;", "return c;"),
+    "e4m3_saturates_one_code_low": ("nearest_of_quotient(e4m3_mag, 127,", "nearest_of_quotient(e4m3_mag, 126,"),
+    "mx_exponent_off_by_one": ("return rco_e8m0_exponent(amax, 2);", "return rco_e8m0_exponent(amax, 1);"),
     "int3_pair_order_swapped": ("4 * (p / 2) + 2 * (e % 2);", "4 * (p / 2) + 2 * (1 - e % 2);"),
 }
 
