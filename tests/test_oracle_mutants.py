@@ -41,6 +41,7 @@ MUTANTS = {
     "minifloat_ties_round_down": ("return (c % 2 == 0) ? c : c + 1;", "return c;"),
     "e4m3_saturates_one_code_low": ("nearest_of_quotient(e4m3_mag, 127,", "nearest_of_quotient(e4m3_mag, 126,"),
     "mx_exponent_off_by_one": ("return rco_e8m0_exponent(amax, 2);", "return rco_e8m0_exponent(amax, 1);"),
+    "fp8_single_plane_order": ("return e < 16 ? 16 * g + e : 1024 + 16 * g + (e - 16);", "return i;"),
     "int3_pair_order_swapped": ("4 * (p / 2) + 2 * (e % 2);", "4 * (p / 2) + 2 * (1 - e % 2);"),
 }
 
