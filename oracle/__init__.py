@@ -81,8 +81,7 @@ def _load():
         "rco_e8m0_decode": (ctypes.c_float, [ctypes.c_uint8]),
         "rco_e4m3_mag_of_quotient": (i32, [ctypes.c_double, ctypes.c_double]),
         "rco_e2m1_mag_of": (i32, [ctypes.c_double]),
-        "rco_int_recip": (ctypes.c_float, [ctypes.c_float]),
-        "rco_int_mag_recip": (i32, [ctypes.c_float, ctypes.c_float, i32]),
+        "rco_int_mag": (i32, [ctypes.c_float, ctypes.c_float, i32]),
         "rco_int_scale_bits": (ctypes.c_uint16, [ctypes.c_float, i32]),
         "rco_fp8_scale": (ctypes.c_float, [ctypes.c_float]),
         "rco_mx_exponent": (i32, [ctypes.c_float]),
@@ -261,7 +260,8 @@ def e2m1_mag_of(v):
 
 
 def int_mag(v_abs, s, qmax):
-    """min(RNE(RN32(|v| * RN32(1/s))), qmax) element-wise (float32 inputs)."""
+    """min(round-half-even(|v| / s), qmax) of the exact quotient, element-wise
+    (float32 |v|, fp16-valued float32 s > 0)."""
     v_abs = np.ascontiguousarray(v_abs, dtype=np.float32)
     s = np.ascontiguousarray(np.broadcast_to(np.asarray(s, dtype=np.float32), v_abs.shape))
     out = np.empty(v_abs.size, dtype=np.int32)

@@ -13,7 +13,8 @@
  * Layout of one 2048-element tile (32-element blocks b = 0..63; element i of
  * the tile lies in block i/32 at position e = i%32):
  *
- * INT codes use the reciprocal rule: magnitude = min(RNE(RN32(|v| * RN32(1/s))), qmax).
+ * INT codes: magnitude = the integer nearest to the exact quotient |v| / s,
+ * ties to even, clamped to qmax.
  *
  *   INT4 (1152 B):  nibble i of bytes [0,1024) (low nibble first) holds
  *                   (sign << 3) | magnitude, magnitude 0..7;
@@ -243,29 +244,23 @@ int rco_e2m1_mag_of(double y_abs)
     return nearest_of_quotient(e2m1_mag, 8, y_abs, 1.0);
 }
 
-/* Reciprocal of a nonzero INT block scale: one IEEE binary32 division. */
-float rco_int_recip(float s)
+/* Symmetric integer magnitude ("symmetric quantization" with a block-level
+ * FP16 scale, QuickReduce INT3 Quantization and Benchmarking on MI355 --
+ * Method): the integer nearest to the exact quotient v_abs / s, ties to the
+ * even integer, clamped to qmax.  Written with products instead of the
+ * quotient: m * s and (m + 1/2) * s have at most 4 + 11 significant bits (s
+ * is an fp16 value, m <= 8), so every product below is exact in binary64 and
+ * every comparison with v_abs (a binary32 value) is exact. */
+int rco_int_mag(float v_abs, float s, int qmax)
 {
-    return 1.0f / s;
-}
-
-/* Symmetric integer magnitude ("symmetric quantization", QuickReduce INT3 ...
- * -- Method), by the reciprocal rule: y = RN32(|v| * r) with r = RN32(1/s),
- * one binary32 multiplication, then the integer nearest to y with ties to
- * even, clamped to qmax.  y is a binary32 value, so floor(y) and y - floor(y)
- * are exact in binary64 and every comparison below is exact. */
-int rco_int_mag_recip(float v_abs, float r, int qmax)
-{
-    const float y = v_abs * r;
-    const double yd = (double)y;
-    if (!(yd < qmax + 0.5)) return qmax;               /* RNE, then clamp (NaN: qmax) */
-    const int k = (int)floor(yd);
-    const double frac = yd - (double)k;
-    int m;
-    if (frac > 0.5)      m = k + 1;
-    else if (frac < 0.5) m = k;
-    else                 m = (k % 2 == 0) ? k : k + 1;
-    return m > qmax ? qmax : m;
+    const double x = v_abs, sd = s;
+    if (!(x < (qmax + 0.5) * sd)) return qmax;          /* clamp (NaN: qmax) */
+    int m = 0;                                          /* m = floor(x / s)  */
+    while ((m + 1) * sd <= x) ++m;
+    const double mid = (m + 0.5) * sd;
+    if (x > mid) return m + 1;
+    if (x < mid) return m;
+    return (m % 2 == 0) ? m : m + 1;                    /* tie: even integer */
 }
 
 /* ------------------------------------------------------------------ */
@@ -467,10 +462,9 @@ static void encode_tile(rco_codec c, const float *v, uint8_t *dst)
                 float sc = rco_f16_to_f32(h);
                 if (sc == 0.0f) continue;                 /* zero block: all bytes 0 */
                 put_u16(sdst, h);
-                const float r = rco_int_recip(sc);
                 for (int e = 0; e < B; ++e)
                     put_code(c, dst, (size_t)B * b + e, signbit(vb[e]) ? 1u : 0u,
-                             (unsigned)rco_int_mag_recip(fabsf(vb[e]), r, qmax));
+                             (unsigned)rco_int_mag(fabsf(vb[e]), sc, qmax));
             } else {                                       /* E8M0: S = 2^ex */
                 int ex = rco_e8m0_exponent(amax, rco_elem_emax(c.format));
                 sdst[0] = (uint8_t)(ex + 127);
@@ -648,7 +642,7 @@ void rco_map_e4m3_mag(const double *num, const double *den, int32_t *y, size_t n
 void rco_map_e2m1_mag(const double *v, int32_t *y, size_t n)
 { for (size_t i = 0; i < n; ++i) y[i] = rco_e2m1_mag_of(v[i]); }
 void rco_map_int_mag(const float *v_abs, const float *s, int qmax, int32_t *y, size_t n)
-{ for (size_t i = 0; i < n; ++i) y[i] = rco_int_mag_recip(v_abs[i], rco_int_recip(s[i]), qmax); }
+{ for (size_t i = 0; i < n; ++i) y[i] = rco_int_mag(v_abs[i], s[i], qmax); }
 void rco_map_int_scale_bits(const float *amax, int qmax, uint16_t *y, size_t n)
 { for (size_t i = 0; i < n; ++i) y[i] = rco_int_scale_bits(amax[i], qmax); }
 void rco_map_fp8_scale(const float *amax, float *y, size_t n)

@@ -7,9 +7,9 @@
  *
  * What it computes (the spec of record, one definition per step):
  *   - block quantization with one scale per 32-element block, symmetric
- *     integer codes (|v| times the binary32 reciprocal of the scale, rounded
- *     half-even) and an FP16 block scale, the 3-bit codes split into a
- *     low-2-bit plane (q2w) and a high-bit plane (q1w)
+ *     integer codes (the exact quotient |v| / s rounded half-even) and an
+ *     FP16 block scale, the 3-bit codes split into a low-2-bit plane (q2w)
+ *     and a high-bit plane (q1w)
  *       [QuickReduce INT3 Quantization and Benchmarking on MI355 -- Method];
  *   - fixed 2048-element tiles that pack to 1152 B (INT4) and 896 B (INT3)
  *       [same page -- Summary];
@@ -100,10 +100,9 @@ float    rco_e5m2_decode(uint8_t code);           /* IEEE-style E5M2     */
 int      rco_e4m3_mag_of_quotient(double num, double den);   /* 0..126 */
 int      rco_e2m1_mag_of(double y_abs);                      /* 0..7   */
 int      rco_e5m2_mag_of_quotient(double num, double den);   /* 0..123 */
-/* INT magnitude by the reciprocal rule: min(RNE(RN32(v_abs * r)), qmax),
- * r = rco_int_recip(s) = RN32(1/s) */
-float    rco_int_recip(float s);
-int      rco_int_mag_recip(float v_abs, float r, int qmax);
+/* INT magnitude: the integer nearest to the exact quotient v_abs / s (s an
+ * fp16 value > 0), ties to even, clamped to qmax */
+int      rco_int_mag(float v_abs, float s, int qmax);
 /* per-block scale rules; amax >= 0 */
 uint16_t rco_int_scale_bits(float amax, int qmax);   /* fp16 bits       */
 float    rco_fp8_scale(float amax);                  /* E4M3, 0 when flushed */

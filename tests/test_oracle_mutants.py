@@ -33,9 +33,10 @@ MUTANTS = {
     "reduce_drops_last_stream": ("for (int s = 1; s < k; ++s)\n                a = a +",
                                  "for (int s = 1; s < k - 1; ++s)\n                a = a +"),
     "reduce_subtracts": ("a = a + decode_elem(", "a = a - decode_elem("),
-    "ties_away_from_zero_int_path": ("else                 m = (k % 2 == 0) ? k : k + 1;",
-                                     "else                 m = k + 1;"),
-    "never_rounds_up": ("if (frac > 0.5)      m = k + 1;", "if (frac > 1.5)      m = k + 1;"),
+    "ties_away_from_zero_int_path": ("return (m % 2 == 0) ? m : m + 1;", "return m + 1;"),
+    "int_truncates": ("const double mid = (m + 0.5) * sd;", "const double mid = (m + 1.0) * sd;"),
+    "int_ties_down_by_reciprocal": ("if (x > mid) return m + 1;\n    if (x < mid) return m;",
+                                    "if (x * (float)(1.0f / s) > m + 0.5) return m + 1;\n    if (x < mid) return m;"),
     "int_scale_over_qmax_plus_one": ("float s32 = amax / (float)qmax;",
                                      "float s32 = amax / (float)(qmax + 1);"),
     "minifloat_ties_round_down": ("return (c % 2 == 0) ? c : c + 1;", "return c;"),

@@ -61,8 +61,8 @@ def test_unpack_equals_brute_decode(fmt):
 
 
 def test_int_magnitude_brute_force():
-    """Reciprocal rule min(RNE(fp32(|v| * fp32(1/s))), qmax) against numpy
-    float32 arithmetic + exact-rational argmin, on fp16 scales (normal and
+    """Round-half-even of the exact quotient |v| / s, clamped to qmax, against
+    an exact-rational argmin over every candidate, on fp16 scales (normal and
     subnormal), random values and values at exact half steps."""
     hbits = RNG.integers(1, 0x7BFF, 4000).astype(np.uint16)
     den = hbits.view(np.float16).astype(np.float32)
@@ -78,27 +78,29 @@ def test_int_magnitude_brute_force():
         assert ours.tolist() == ref
 
 
-def test_reciprocal_rule_differs_from_exact_quotient_only_at_half_steps():
-    """Where the reciprocal rule and round-half-even of the exact quotient
-    disagree, v/s lies within 2^-21 (relative) of a half-integer and the two
-    answers are neighbours."""
-    from fractions import Fraction
-    hbits = RNG.integers(0x0400, 0x7BFF, 20000).astype(np.uint16)          # normal fp16 scales
-    s = hbits.view(np.float16).astype(np.float32)
-    v = (RNG.uniform(0, 3.5, 20000) * s).astype(np.float32)
-    k = RNG.integers(0, 3, 5000)
-    v[:5000] = ((k + 0.5) * s[:5000].astype(np.float64)).astype(np.float32)  # many exact ties
-    rec = oracle.int_mag(v, s, 3)
-    diff = 0
-    for i in range(v.size):
-        qe = Fraction(float(v[i])) / Fraction(float(s[i]))
-        ex = brute.nearest_code(qe, [Fraction(j) for j in range(4)])
-        if ex != rec[i]:
-            diff += 1
-            assert abs(ex - rec[i]) == 1
-            m = min(ex, rec[i]) + Fraction(1, 2)
-            assert abs(qe - m) <= qe * Fraction(1, 2 ** 21)
-    assert diff > 0          # ties do occur, so the two rules are genuinely different
+@pytest.mark.parametrize("qmax", [3, 7])
+def test_int_half_steps_by_construction(qmax):
+    """v = (k + 1/2) s exactly (a binary32 value: at most 4 + 11 significant
+    bits) rounds to the even one of k, k + 1; the binary32 neighbours of that
+    v round away from the half step, to k + 1 above it and k below.  The
+    expected codes follow from the definition alone."""
+    hb = np.concatenate([RNG.integers(0x0001, 0x0400, 300),          # subnormal fp16 scales
+                         RNG.integers(0x0400, 0x7BFF, 1500)]).astype(np.uint16)
+    s = hb.view(np.float16).astype(np.float32)
+    for k in range(qmax):
+        v = ((k + 0.5) * s.astype(np.float64)).astype(np.float32)
+        assert np.array_equal(v.astype(np.float64), (k + 0.5) * s.astype(np.float64))
+        even = k if k % 2 == 0 else k + 1
+        assert (oracle.int_mag(v, s, qmax) == even).all()
+        up = np.nextafter(v, np.float32(np.inf))
+        dn = np.nextafter(v, np.float32(0))
+        assert (oracle.int_mag(up, s, qmax) == k + 1).all()
+        assert (oracle.int_mag(dn, s, qmax) == k).all()
+    # beyond qmax + 1/2 the code saturates; just below it stays qmax
+    v = ((qmax + 0.5) * s.astype(np.float64)).astype(np.float32)
+    assert (oracle.int_mag(v, s, qmax) == qmax).all()
+    assert (oracle.int_mag(v * np.float32(40), s, qmax) == qmax).all()
+    assert (oracle.int_mag(np.nextafter(v, np.float32(0)), s, qmax) == qmax).all()
 
 
 def test_scale_rules_vs_numpy():
@@ -118,26 +120,38 @@ def test_scale_rules_vs_numpy():
 
 @pytest.mark.parametrize("fmt,qmax", [("int4", 7), ("int3", 3)])
 def test_int_half_step_bound_and_max_code(fmt, qmax):
-    """|v - d| <= s/2 up to one binary32 rounding of v/s (slack |v| 2^-22)
-    for every element of a block whose fp16 scale is normal and unsaturated;
-    the element attaining the block max gets code +-qmax."""
-    x = RNG.standard_normal(2048 * 8).astype(np.float32) * np.float32(3.0)
-    p = oracle.quantize_pack(codec(fmt), x)
-    d = oracle.unpack_dequant(codec(fmt), p, x.size)
-    tb = oracle.tile_bytes(codec(fmt))
-    soff = 1024 if fmt == "int4" else 768
-    strict = 0
-    for t in range(8):
-        s = np.frombuffer(p[t * tb + soff: t * tb + soff + 128].tobytes(), dtype=np.float16).astype(np.float64)
-        for b in range(64):
-            sl = slice(t * 2048 + 32 * b, t * 2048 + 32 * b + 32)
-            xv = x[sl].astype(np.float64)
-            err = np.abs(xv - d[sl].astype(np.float64))
-            assert (err <= s[b] / 2 + np.abs(xv) * 2.0 ** -22).all()
-            strict += int((err <= s[b] / 2).all())
-            j = np.argmax(np.abs(x[sl]))
-            assert abs(d[sl][j]) == qmax * s[b]
-    assert strict >= 8 * 64 - 4
+    """|v - d| <= s/2 for every element of a block whose fp16 scale is normal
+    and unsaturated, on full-mantissa binary32 inputs and on bf16 inputs with
+    planted exact half steps; where |v| / s is exactly k + 1/2 the code is the
+    even neighbour; the element attaining the block max gets code +-qmax."""
+    from fractions import Fraction
+    x32 = RNG.standard_normal(2048 * 8).astype(np.float32) * np.float32(3.0)
+    xb = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(RNG.standard_normal(2048 * 8).astype(np.float32)))
+    # the first two tiles: blocks whose maximum is qmax * 2^j (so s = 2^j
+    # exactly) and whose other elements are half steps +-(k + 1/2) 2^j
+    pw = 2.0 ** RNG.integers(-4, 4, 128)
+    xb[:4096] = (RNG.integers(0, qmax, 4096) + 0.5) * np.repeat(pw, 32) * RNG.choice([-1.0, 1.0], 4096)
+    xb[:4096:32] = qmax * pw
+    ties = 0
+    for x in (x32, xb.astype(np.float32)):
+        p = oracle.quantize_pack(codec(fmt), x)
+        d = oracle.unpack_dequant(codec(fmt), p, x.size)
+        tb = oracle.tile_bytes(codec(fmt))
+        soff = 1024 if fmt == "int4" else 768
+        for t in range(8):
+            s = np.frombuffer(p[t * tb + soff: t * tb + soff + 128].tobytes(), dtype=np.float16).astype(np.float64)
+            for b in range(64):
+                sl = slice(t * 2048 + 32 * b, t * 2048 + 32 * b + 32)
+                xv = x[sl].astype(np.float64)
+                err = np.abs(xv - d[sl].astype(np.float64))
+                assert (err <= s[b] / 2).all()
+                j = np.argmax(np.abs(x[sl]))
+                assert abs(d[sl][j]) == qmax * s[b]
+                for e in np.nonzero(err == s[b] / 2)[0]:
+                    q = Fraction(float(d[sl][e])) / Fraction(float(s[b]))
+                    assert q.denominator == 1 and q.numerator % 2 == 0
+                    ties += 1
+    assert ties > 100          # the planted half steps are there
 
 
 def test_fp8_error_bound():
