@@ -37,10 +37,10 @@
  *
  * Numerics (bit-exact with the CPU oracle under oracle/):
  *   INT4/INT3, FP16 scale: s = fp16(min(fp32(absmax / qmax), 65504)) with
- *     qmax = 7 / 3; magnitude = min(round-half-even(fp32(|v| * fp32(1 / s))),
- *     qmax) (one binary32 multiply by the correctly rounded reciprocal, then
- *     the nearest integer), sign = sign bit of v; a block whose s is 0 is
- *     stored as all-zero bytes.
+ *     qmax = 7 / 3; magnitude = min(round-half-even(|v| / s), qmax) of the
+ *     exact quotient (so |v - q s| <= s / 2 for every unclamped element, and
+ *     exact half steps go to the even integer), sign = sign bit of v; a block
+ *     whose s is 0 is stored as all-zero bytes.
  *   FP8, FP32 scale: s = fp32(absmax / fmax) (fmax = 448 for E4M3, 57344 for
  *     E5M2), flushed to 0 below FLT_MIN (block stored as zeros); code = the
  *     round-to-nearest-even code of the exact quotient v / s, saturating at
@@ -115,7 +115,10 @@ typedef enum {
  * Summary. */
 size_t rc_tile_bytes(rc_codec c);
 
-/* ceil(n / 2048) * rc_tile_bytes(c). */
+/* Bytes of a packed stream of n elements: ceil(n / 2048) * rc_tile_bytes(c)
+ * (fixed-size tiles, the unit the QuickReduce INT3 page counts in -- Summary:
+ * 1152 B per INT4 tile, 896 B per INT3 tile); 0 when the codec is
+ * unsupported.  Pure arithmetic: no HIP call, callable without a GPU. */
 size_t rc_packed_bytes(rc_codec c, size_t n);
 
 /* Block-quantize n elements of `in` (dtype in_t: bf16, fp16 or fp32) and pack
@@ -127,9 +130,14 @@ size_t rc_packed_bytes(rc_codec c, size_t n);
 rc_status rc_quantize_pack(rc_codec c, rc_dtype in_t, const void *in, size_t n,
                            void *out, void *stream);
 
-/* Decode n elements of the packed stream `in` to dtype out_t (fp32 exact; bf16
- * and fp16 rounded to nearest even, fp16 overflow to +-inf) at `out`
- * (n * sizeof(out_t) bytes). */
+/* Decode n elements of the packed stream `in` (rc_packed_bytes(c, n) bytes)
+ * to dtype out_t at `out` (n * sizeof(out_t) bytes): each value is code times
+ * block scale computed in FP32 (exact for INT/FP16 and E2M1/E8M0, one binary32
+ * product for FP8 with an FP32 scale), then written as fp32, or rounded to
+ * bf16 / fp16 (nearest even, fp16 overflow to +-inf).  This is the receiving
+ * side's decode: payloads travel compressed and the arithmetic on them stays
+ * in FP32 (RCCLX -- Low-Precision Collectives; QuickReduce INT3 page --
+ * Method, FP16 block scale).  Errors as for rc_quantize_pack. */
 rc_status rc_unpack_dequant(rc_codec c, const void *in, size_t n, rc_dtype out_t,
                             void *out, void *stream);
 
@@ -169,14 +177,16 @@ rc_status rc_allreduce_emulate(rc_codec c, rc_dtype dt, const void *const *msgs,
  * (rc_quantize_pack of its rows * cols elements with {MXFP4, E8M0, 32}), the
  * consumer of the packed layout ("ML-SpecQD: Multi-Level Speculative Decoding
  * with Quantized Drafts", abstract: MXFP4 weights direct-cast from BF16).
- * cols must be a positive multiple of 2048 (row r = tiles r*cols/2048 ...),
+ * cols must be a positive multiple of 2048 (row r = tiles r*cols/2048 ...)
+ * with cols * sizeof(x_t) < 2^32 bytes (x is addressed with 32-bit offsets),
  * else RC_ERR_RANGE.  x: cols elements of x_t; y: rows elements of y_t.
- * Summation order (bit-exact with the oracle): lane l of a row owns block
- * 64j + l of the row's tile j; a block term is an fp32 fma chain over the
- * block's 32 elements in order from +0, times 2^e (one rounding); the lane
- * adds its block terms in tile order; the 64 lane sums are added by an xor
- * butterfly (offsets 32, 16, 8, 4, 2, 1); y is rounded to y_t (RNE).
- * Pointers are device pointers, 16-byte aligned. */
+ * Accuracy: the pages fix no summation order, so the result is specified by
+ * a bound, not an order: the binary32 value s computed for row r satisfies
+ *   |s - sum_j W[r][j] x[j]| <= (38 + cols/2048) * 2^-24 * sum_j |W[r][j] x[j]|
+ * (plus 2^-143 for block terms below 2^-126), every term passing through at
+ * most that many binary32 roundings; y[r] = s rounded to y_t (nearest even).
+ * The order is fixed by the kernel, so results are deterministic from call
+ * to call.  Pointers are device pointers, 16-byte aligned. */
 rc_status rc_mxfp4_gemv(const void *w, size_t rows, size_t cols, rc_dtype x_t, const void *x,
                         rc_dtype y_t, void *y, void *stream);
 

@@ -11,6 +11,7 @@ over threads only to bound wall time; results are identical).
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
@@ -86,7 +87,6 @@ def _load():
         "rco_fp8_scale": (ctypes.c_float, [ctypes.c_float]),
         "rco_mx_exponent": (i32, [ctypes.c_float]),
         "rco_e5m2_decode": (ctypes.c_float, [ctypes.c_uint8]),
-        "rco_mxfp4_gemv": (i32, [vp, sz, sz, i32, vp, i32, vp]),
         "rco_e5m2_mag_of_quotient": (i32, [ctypes.c_double, ctypes.c_double]),
         "rco_elem_emax": (i32, [i32]),
         "rco_e8m0_exponent": (i32, [ctypes.c_float, i32]),
@@ -249,6 +249,18 @@ def bf16_bits_to_f32(h):
     return _map("rco_map_bf16_to_f32", np.float32, np.asarray(h, dtype=np.uint16))
 
 
+def widen_to_f32(x: np.ndarray, dtype: int | None = None) -> np.ndarray:
+    """x (float32, float16, or uint16 bf16 bits with dtype=DT_BF16) widened
+    exactly to float32."""
+    x = np.ascontiguousarray(x)
+    dt = _dtype_code(x, dtype)
+    if dt == DT_FP32:
+        return x.astype(np.float32)
+    if dt == DT_FP16:
+        return f16_bits_to_f32(x.view(np.uint16))
+    return bf16_bits_to_f32(x.view(np.uint16))
+
+
 def e4m3_mag_of_quotient(num, den):
     num = np.asarray(num, dtype=np.float64)
     den = np.broadcast_to(np.asarray(den, dtype=np.float64), num.shape)
@@ -346,14 +358,25 @@ def allreduce_emulate(c, msgs, dtype: int, two_shot: bool = True):
     return f32_to_bf16_bits(sums), packed
 
 
-def mxfp4_gemv(w_packed: np.ndarray, rows: int, cols: int, x: np.ndarray, x_dtype: int | None = None,
-               y_dtype: int = DT_FP32) -> np.ndarray:
-    """y = W x on an MXFP4-packed row-major matrix (see rco_mxfp4_gemv for
-    the summation order).  x: float32 / float16 / uint16 bf16 bits."""
+def mxfp4_gemv(w_packed: np.ndarray, rows: int, cols: int, x: np.ndarray, x_dtype: int | None = None):
+    """y = W x on an MXFP4-packed row-major matrix (row r = tiles r*cols/2048
+    ...), by its definition: the dot product of each row's decoded weights
+    with x, summed exactly.  Weights decode exactly to binary32 (E2M1 value
+    times 2^e, unpack_dequant), x widens exactly, and each product is exact in
+    binary64 (at most 2 + 24 significant bits, exponents within range);
+    math.fsum adds them exactly and rounds once to binary64.  Returns
+    (y, mag): the float64 sums and the float64 sums of |W_ij x_j|, the scale
+    of the rounding bound an implementation is held to.  The pages fix no
+    summation order ("ML-SpecQD: Multi-Level Speculative Decoding with
+    Quantized Drafts", abstract: MXFP4 weights direct-cast from BF16)."""
+    if cols <= 0 or cols % TILE:
+        raise ValueError("cols must be a positive multiple of 2048")
     w_packed = np.ascontiguousarray(w_packed, dtype=np.uint8)
-    x = np.ascontiguousarray(x)
-    if w_packed.size < packed_bytes(MXFP4, rows * cols) or x.size < cols:
+    if w_packed.size < packed_bytes(MXFP4, rows * cols) or np.asarray(x).size < cols:
         raise ValueError("w_packed or x too small")
-    y = np.empty(rows, dtype=np.float32 if y_dtype == DT_FP32 else np.uint16)
-    _check(_load().rco_mxfp4_gemv(_ptr(w_packed), rows, cols, _dtype_code(x, x_dtype), _ptr(x), y_dtype, _ptr(y)))
-    return y.view(np.float16) if y_dtype == DT_FP16 else y
+    wd = unpack_dequant(MXFP4, w_packed, rows * cols, DT_FP32).reshape(rows, cols).astype(np.float64)
+    xd = widen_to_f32(np.asarray(x)[:cols], x_dtype).astype(np.float64)
+    prod = wd * xd
+    y = np.array([math.fsum(r) for r in prod], dtype=np.float64)
+    mag = np.array([math.fsum(r) for r in np.abs(prod)], dtype=np.float64)
+    return y, mag

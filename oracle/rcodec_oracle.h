@@ -79,13 +79,6 @@ int rco_dequant_reduce_requant_tiles(rco_codec c, const void *const *ins, int k,
                                      size_t n, void *out, float *sum_out,
                                      size_t t0, size_t t1);
 
-/* y = W x for a row-major rows x cols MXFP4-packed matrix (cols a multiple
- * of 2048), in the summation order defined in the .c file; x has cols
- * elements of x_dtype, y rows elements of y_dtype.  RCO_ERR_RANGE when cols
- * is not a positive multiple of 2048. */
-int rco_mxfp4_gemv(const void *w, size_t rows, size_t cols, int x_dtype, const void *x,
-                   int y_dtype, void *y);
-
 /* ---- scalar building blocks, exported so the pins can test them ------ */
 float    rco_bf16_to_f32(uint16_t h);
 uint16_t rco_f32_to_bf16(float x);                /* RNE, IEEE overflow  */

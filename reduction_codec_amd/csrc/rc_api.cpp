@@ -121,6 +121,9 @@ rc_status rc_mxfp4_gemv(const void* w, size_t rows, size_t cols, rc_dtype x_t, c
 {
     if (!dtype_ok(x_t) || !dtype_ok(y_t)) return RC_ERR_UNSUPPORTED;
     if (cols == 0 || cols % RC_TILE_ELEMS != 0 || cols > kMaxElems) return RC_ERR_RANGE;
+    // x is read through one buffer descriptor with 32-bit byte offsets
+    const size_t xbytes = cols * (x_t == RC_DT_FP32 ? 4u : 2u);
+    if (xbytes >= ((size_t)1 << 32)) return RC_ERR_RANGE;
     if (rows == 0) return RC_OK;
     if (rows > kMaxElems / cols) return RC_ERR_RANGE;
     if (!w || !x || !y) return RC_ERR_NULL;

@@ -10,15 +10,21 @@
 // (E4M3) conversion instructions:
 //   * INT3 magnitudes 0..3 are the E2M1 codes of 0, 0.5, 1, 1.5, so a
 //     sign/magnitude INT3 code is an E2M1 nibble of value q/2 with bit 2
-//     clear.  Quantize = E2M1 conversion of x * (r/2), r = fp32(1/s);
+//     clear.  Quantize = E2M1 conversion of x / (2s) (formed as below);
 //     dequantize = E2M1 conversion back, times 2s.
 //   * INT4 magnitudes 0..7 are the E4M3 subnormals m * 2^-9, so a sign /
 //     magnitude INT4 code is an E4M3 byte with exponent 0.
-// Both conversions round their binary32 input to nearest even, which is the
-// INT rounding rule itself: magnitude = min(RNE(fp32(|x| * fp32(1/s))), qmax).
-// Below the clamp the code's low bit is the parity of the integer, so ties
-// go the same way.  For a normal, unsaturated fp16 scale |x| * r <= qmax +
-// 0.004, so no clamp is needed; for a subnormal or saturated scale the clamp
+// Both conversions round their binary32 input to nearest even.  The INT rule
+// is round-half-even of the exact quotient |x| / s; the conversions are fed
+// y = fma(x, r, x * r_lo), where r = 1/s rounded down and r_lo ~ 1/s - r
+// (>= 0, so y keeps the sign of x, -0 included): y is within 2^-44 |x|/s of
+// the quotient before its one
+// rounding, while a quotient that is not exactly a half-integer lies more
+// than half a binary32 ulp (plus that margin) away from one, so y sits on the
+// same side of every half step as the quotient, and exact half steps stay
+// exact (then ties go to even: below the clamp the code's low bit is the
+// parity of the integer).  For a normal, unsaturated fp16 scale y <= qmax +
+// 1/2, so no clamp is needed; for a subnormal or saturated scale the clamp
 // is applied to the packed codes (every code above qmax becomes qmax).
 #pragma once
 
@@ -182,7 +188,8 @@ __device__ __forceinline__ float pair_swap(float x)
 struct IntScale {
     float s;          // fp16 scale as binary32 (exact)
     uint32_t bits;    // fp16 bit pattern
-    float r;          // fp32(1/s) (IEEE division), 0 for a zero block
+    float r;          // 1/s rounded down, 0 for a zero block
+    float r_lo;       // RN((1 - s r) r) ~ 1/s - r >= 0, 0 for a zero block
     bool zero;        // s == 0: the block is stored as zeros
     bool abnormal;    // subnormal fp16 or saturated: codes need the clamp
 };
@@ -223,6 +230,15 @@ __device__ __forceinline__ IntScale int_scale(float a)
     r.zero = (r.s == 0.0f);
     r.abnormal = sat || (!r.zero && r.s < 0x1p-14f);
     r.r = r.zero ? 0.0f : recip_f16_scale(r.s);
+    // The high part is taken rounded down, r <= 1/s, so that the low part is
+    // never negative: then x r_lo keeps the sign of x even for x = -0 (a
+    // negative r_lo would turn -0 * r_lo into +0 and lose the sign of a -0
+    // element).  1 - s r is exact (at most 10 significant bits, |.| < 2^-22);
+    // times r it gives the low part of 1/s to within 2^-45 / s in all.
+    float e = __builtin_fmaf(-r.s, r.r, 1.0f);
+    r.r = __uint_as_float(__float_as_uint(r.r) - (e < 0.0f ? 1u : 0u));
+    e = __builtin_fmaf(-r.s, r.r, 1.0f);
+    r.r_lo = e * r.r;
     return r;
 }
 
@@ -271,11 +287,12 @@ __device__ __forceinline__ int e8m0_exponent(float a)
 }
 
 // Per-block encode data: the stored scale bits and the element multiplier
-// (INT/FP16: fp32(1/s); E8M0: 2^-e; FP8 with FP32/FP16 scale: s itself;
-// E2M1: 2^e, the conversion's scale operand).
+// (INT/FP16: 1/s rounded down, with m_lo >= 0 its low part; E8M0: 2^-e; FP8 with
+// FP32/FP16 scale: s itself; E2M1: 2^e, the conversion's scale operand).
 struct EncScale {
     uint32_t bits;
     float m;
+    float m_lo;      // INT/FP16 only
     bool zero;       // FP16/FP32 scale 0: the block is stored as zeros
     bool clamp;      // codes may exceed the format's largest magnitude
 };
@@ -286,11 +303,13 @@ __device__ __forceinline__ EncScale enc_scale(float a)
     EncScale r;
     r.zero = false;
     r.clamp = false;
+    r.m_lo = 0.0f;
     if constexpr (FMT == 1 || FMT == 2) {
         if constexpr (SC == kS16) {
             const IntScale sc = int_scale<Fmt<FMT>::qmax>(a);
             r.bits = sc.bits;                            // +0 for a zero block (a >= 0)
             r.m = sc.r;
+            r.m_lo = sc.r_lo;
             r.zero = sc.zero;
             r.clamp = sc.abnormal;
         } else {
@@ -383,28 +402,32 @@ __device__ __forceinline__ uint32_t int3_clamp_word(uint32_t w)
     return (w & 0x88888888u) | (w & 0x33333333u) | (big * 3u);
 }
 
-// INT3 codes: E2M1 nibbles of x * m / 2 (m = fp32(1/s) or 2^-e): RNE, the
-// low code bit is the integer's parity below 2; clamped when a block may
-// exceed 3.
+// INT3 codes: E2M1 nibbles of x / (2 s), formed as fma(x, r/2, x r_lo/2)
+// (FP16 scale) or x 2^-e / 2 (E8M0): RNE, the low code bit is the integer's
+// parity below 2; clamped when a block may exceed 3.
 // E8M0 scales (P2): the multiplier 2^-e is a power of two, so the
 // conversion's own scale operand 2^(e+1) divides exactly and no multiply is
 // needed (e <= 126 for finite data, so the operand is finite).
 template <int H, bool P2>
 __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const EncScale (&sc)[H])
 {
-    float r2[H];
+    float r2[H], l2[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h)
+    for (int h = 0; h < H; ++h) {
         r2[h] = P2 ? __builtin_ldexpf(2.0f, (int)sc[h].bits - 127)   // 2^(e+1), the operand
                    : 0.5f * sc[h].m;                                  // r/2, exact
+        l2[h] = 0.5f * sc[h].m_lo;                                    // r_lo/2, exact
+    }
     uint32_t N[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         uint32_t w = 0u;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const float r = r2[H == 2 ? b / 2 : 0];
-            const float x0 = P2 ? v[8 * b + g] : v[8 * b + g] * r, x1 = P2 ? v[8 * b + 4 + g] : v[8 * b + 4 + g] * r;
+            const float r = r2[H == 2 ? b / 2 : 0], l = l2[H == 2 ? b / 2 : 0];
+            const float y0 = v[8 * b + g], y1 = v[8 * b + 4 + g];
+            const float x0 = P2 ? y0 : __builtin_fmaf(y0, r, y0 * l);
+            const float x1 = P2 ? y1 : __builtin_fmaf(y1, r, y1 * l);
             // the first conversion starts from x0's own bits: every byte of w
             // is written by the four conversions, and no register is cleared
             w = fp4_enc(b == 0 ? __float_as_uint(x0) : w, x0, x1, P2 ? r : 1.0f, b);
@@ -462,23 +485,30 @@ __device__ __forceinline__ uint32_t int4_clamp_bytes(uint32_t x)
     return x | big | (big << 1) | (big << 2);
 }
 
-// INT4 codes: E4M3 subnormal bytes of x * m * 2^-9 (RNE), clamped when a
-// block may exceed 7.
+// INT4 codes: E4M3 subnormal bytes of x / s * 2^-9 (RNE), formed as
+// fma(x, r 2^-9, x r_lo 2^-9) (FP16 scale) or x 2^-e 2^-9 (E8M0, m_lo = 0),
+// clamped when a block may exceed 7.
 template <int H>
 __device__ __forceinline__ void int4_encode(const float (&v)[32], const EncScale (&sc)[H], uint32_t (&D)[4])
 {
-    float r9[H];
+    float r9[H], l9[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) r9[h] = sc[h].m * 0x1p-9f;               // exact
+    for (int h = 0; h < H; ++h) {
+        r9[h] = sc[h].m * 0x1p-9f;                                       // exact
+        l9[h] = sc[h].m_lo * 0x1p-9f;                                    // exact (>= 2^-50 or 0)
+    }
     // word d's even elements 0,2,4,6 in the bytes of xe[d], odd 1,3,5,7 in xo[d]
     uint32_t xe[4], xo[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const float r = r9[H == 2 ? d / 2 : 0];
+        const float r = r9[H == 2 ? d / 2 : 0], l = l9[H == 2 ? d / 2 : 0];
         const float* y = v + 8 * d;
-        const float e0 = y[0] * r, o0 = y[1] * r;   // first conversions start from their own bits
-        xe[d] = fp8_pair(y[4] * r, y[6] * r, fp8_pair(e0, y[2] * r, __float_as_uint(e0), false), true);
-        xo[d] = fp8_pair(y[5] * r, y[7] * r, fp8_pair(o0, y[3] * r, __float_as_uint(o0), false), true);
+        float q[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = __builtin_fmaf(y[j], r, y[j] * l);
+        // first conversions start from their own bits
+        xe[d] = fp8_pair(q[4], q[6], fp8_pair(q[0], q[2], __float_as_uint(q[0]), false), true);
+        xo[d] = fp8_pair(q[5], q[7], fp8_pair(q[1], q[3], __float_as_uint(q[1]), false), true);
     }
     bool clamp = sc[0].clamp;
     if constexpr (H == 2) clamp = clamp || sc[1].clamp;

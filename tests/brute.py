@@ -437,31 +437,19 @@ def rn32(q: Fraction) -> Fraction:
     return sign * Fraction(k) / scale
 
 
-def gemv_mxfp4(w_packed: bytes, rows: int, cols: int, x: np.ndarray):
-    """y = W x in the defined order: per block an fma chain (exact product,
-    one rounding per step) from +0, times 2^e rounded once; per lane the
-    block terms of its tiles in tile order; then the xor butterfly over the
-    64 lanes with offsets 32, 16, 8, 4, 2, 1.  Returns float32 values."""
+def gemv_mxfp4_exact(w_packed: bytes, rows: int, cols: int, x: np.ndarray):
+    """y = W x in exact rationals: every weight decoded from its nibble and
+    E8M0 byte (decode_codec), every x value as a Fraction, the row sum exact.
+    Returns a list of Fractions."""
     tb = codec_tile_bytes((4, 3, 32))
     T = cols // TILE
     xs = [Fraction(float(v)) for v in np.asarray(x, dtype=np.float32)]
     out = []
     for r in range(rows):
-        lane = []
-        for l in range(64):
-            acc = None
-            for j in range(T):
-                tile = w_packed[(r * T + j) * tb:(r * T + j + 1) * tb]
-                p = Fraction(0)
-                for e in range(32):
-                    i = 32 * l + e
-                    nb = (tile[i // 2] >> (4 * (i % 2))) & 15
-                    code = -E2M1[nb & 7] if nb & 8 else E2M1[nb & 7]
-                    p = rn32(p + code * xs[j * TILE + i])
-                t = rn32(p * Fraction(2) ** (tile[1024 + l] - 127))
-                acc = t if acc is None else rn32(acc + t)
-            lane.append(acc)
-        for off in (32, 16, 8, 4, 2, 1):
-            lane = [rn32(lane[l] + lane[l ^ off]) for l in range(64)]
-        out.append(np.float32(float(lane[0])))
-    return np.array(out, dtype=np.float32)
+        acc = Fraction(0)
+        for j in range(T):
+            d = decode_codec((4, 3, 32), w_packed[(r * T + j) * tb:(r * T + j + 1) * tb])
+            for i in range(TILE):
+                acc += Fraction(float(d[i])) * xs[j * TILE + i]
+        out.append(acc)
+    return out

@@ -198,3 +198,17 @@ def test_mxfp4_gemv_error_paths():
     assert g(M, 4, 4096, 3, A, 1, A) == rca.ERR_ALIGN
     assert g(A, 4, 4096, 3, M, 1, A) == rca.ERR_ALIGN
     assert g(A, 1 << 40, 4096, 3, A, 1, A) == rca.ERR_RANGE
+
+
+def test_mxfp4_gemv_rejects_x_of_4_gib_or_more():
+    """x is addressed with 32-bit byte offsets: cols * sizeof(x) >= 2^32 is
+    refused before any HIP call (fp32 x from 2^30 columns, 16-bit x from
+    2^31), and the largest accepted widths still pass validation (rows = 0)."""
+    l = rca.lib()
+    g = lambda rows, cols, xt: l.rc_mxfp4_gemv(A, rows, cols, xt, A, 1, A, None)
+    assert g(1, 1 << 30, 1) == rca.ERR_RANGE          # fp32: exactly 4 GiB
+    assert g(1, 1 << 31, 3) == rca.ERR_RANGE          # bf16: exactly 4 GiB
+    assert g(1, 1 << 31, 2) == rca.ERR_RANGE          # fp16
+    assert g(1, (1 << 30) + 2048, 1) == rca.ERR_RANGE
+    assert g(0, (1 << 30) - 2048, 1) == rca.OK         # largest fp32 width, nothing to do
+    assert g(0, (1 << 31) - 2048, 3) == rca.OK

@@ -1,0 +1,53 @@
+"""Proofs, on the CPU, of the binary32 sequences the gfx950 kernels use in
+place of IEEE division (tests/device_arith.c restates each sequence with C's
+fmaf and compares it with the exact rule it stands for):
+
+* ``div``: a * RN(1/B) plus one residual correction equals the IEEE quotient
+  a / B for every finite binary32 a and B = 3, 7, 448, 57344 (the INT and FP8
+  block-scale divisions);
+* ``recip``: the hardware reciprocal (either binary32 neighbour of 1/s) plus
+  one Newton step is RN(1/s) for every positive finite fp16 scale s;
+* ``int``: INT3 / INT4 codes from fma(x, r, x r_lo) and the RNE conversions
+  equal round-half-even of the exact quotient x / s -- every fp16 scale with
+  every bf16 x a block can hold, binary32 x within 16 ulp of every half step
+  of every scale, random binary32 x -- while the single product x r differs
+  there (control);
+* ``fp8``: the round-to-odd quotient sequence followed by the RNE conversion
+  equals the RNE E4M3 / E5M2 code of the exact quotient next to every
+  rounding midpoint, for FP32 scales (also below 2^-64) and every fp16 scale.
+
+The scale rules are those of "QuickReduce INT3 Quantization and Benchmarking
+on MI355" (Method: block FP16 scale) and "RCCLX: Innovating GPU
+communications on AMD platforms" (Low-Precision Collectives: FP8 with FP32
+computation).  Nothing here touches a GPU.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    if shutil.which("gcc") is None:
+        pytest.skip("needs gcc")
+    exe = tmp_path_factory.mktemp("device_arith") / "device_arith"
+    r = subprocess.run(["gcc", "-std=c11", "-O2", "-Wall", "-ffp-contract=off", "-fno-fast-math", "-pthread",
+                        "-o", str(exe), os.path.join(HERE, "device_arith.c"), "-lm"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return str(exe)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("check", ["recip", "div", "int", "fp8"])
+def test_device_arithmetic_equals_exact_rule(checker, check):
+    threads = str(min(16, os.cpu_count() or 4))
+    r = subprocess.run([checker, check, threads], capture_output=True, text=True, timeout=900)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    lines = [ln for ln in r.stdout.splitlines() if "cases" in ln]
+    assert lines and all(" differ 0" in ln for ln in lines if "must differ" not in ln)

@@ -58,6 +58,8 @@ def mixed(n: int, seed: int, dt: str) -> np.ndarray:
             step = np.float32(2.0 ** r.integers(-6, 6))
             v[sl] = (r.integers(-7, 8, m) * step / 2).astype(np.float32)        # half-step ties
             v[sl.start] = 7 * step
+            if m > 2:
+                v[sl.start + 2] = -0.0                                           # -0 inside a live block
         elif k == 2:
             v[sl] *= np.float32(1e-5)
         elif k == 3:
@@ -363,7 +365,7 @@ def test_config_mxfp4_bf16_weight_4096():
 
 # ----------------------------------------- size sweep, sampled tiles ----
 
-SWEEP_MIB = [1, 4, 16, 64, 256, 1024]
+SWEEP_MIB = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]
 
 
 def sample_tiles(tiles: int, rng) -> list:
@@ -376,8 +378,10 @@ def sample_tiles(tiles: int, rng) -> list:
 @pytest.mark.parametrize("fmt", ["int4", "int3"])
 def test_sweep_sampled_tiles(fmt, mib):
     """Student-t (nu=4) bf16 messages at full size in the launch shape the
-    benchmark uses: quantize_pack of the message and a K=4 reduce of four
-    tile-shifted messages, checked on sampled tiles the oracle computes."""
+    benchmark uses: quantize_pack of the message, a K=4 reduce of four
+    tile-shifted messages and unpack_dequant of the reduced stream to bf16,
+    checked on sampled tiles (first, middle, last and 40 random) the oracle
+    computes."""
     n = mib * (1 << 20) // 2
     say(f"case sweep fmt={fmt} size={mib}MiB")
     base = datagen.bf16_student4(mib * (1 << 20) + 3 * 4096)        # n + 3 tiles
@@ -405,7 +409,14 @@ def test_sweep_sampled_tiles(fmt, mib):
     for t in picks:
         oracle.dequant_reduce_requant(oc, ref_packed, n, tiles=(t, t + 1), out=refo)
         assert np.array_equal(hout[t * tb:(t + 1) * tb], refo[t * tb:(t + 1) * tb]), f"reduce tile {t}"
-    del dev_packed, out
+    del dev_packed
+    say(f"case sweep fmt={fmt} size={mib}MiB unpack")
+    y = rca.unpack_dequant(out, c, n, torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+    for t in picks:
+        m = min(2048, n - t * 2048)
+        ref_y = oracle.unpack_dequant(oc, refo[t * tb:(t + 1) * tb], m, oracle.DT_BF16)
+        assert np.array_equal(y[t * 2048:t * 2048 + m], ref_y), f"unpack tile {t}"
+    del out, y
     torch.cuda.empty_cache()
 
 
@@ -553,35 +564,77 @@ def test_allreduce_emulate_bit_exact(fmt, dt, two_shot, k):
 
 # ------------------------------------------------------------ MXFP4 GEMV ----
 
-@pytest.mark.parametrize("rows,cols", [(1, 2048), (7, 2048), (9, 4096), (33, 6144), (5, 8192)])
+def gemv_bound(y: np.ndarray, exact: np.ndarray, mag: np.ndarray, cols: int, what: str):
+    """|y - W x| <= (38 + T) 2^-24 sum |W_ij x_j| (T = cols / 2048), the
+    tolerance of rc_mxfp4_gemv: every term passes through at most 38 + T
+    binary32 roundings on its way to y, whatever the summation order.  A tiny
+    absolute term covers block terms that underflow below 2^-126."""
+    T = cols // 2048
+    err = np.abs(y.astype(np.float64) - exact)
+    tol = (38 + T) * 2.0 ** -24 * mag + 64 * 2.0 ** -149
+    bad = np.nonzero(~(err <= tol))[0]
+    if bad.size:
+        show = [(int(i), float(y[i]), float(exact[i]), float(err[i] / max(mag[i], 1e-300))) for i in bad[:6]]
+        raise AssertionError(f"{what}: {bad.size} rows beyond the bound; (row, y, exact, err/sum|Wx|): {show}")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 2048), (7, 2048), (9, 4096), (33, 6144), (5, 10240), (300, 8192)])
 @pytest.mark.parametrize("xt", DTYPES)
-def test_mxfp4_gemv_bit_exact(rows, cols, xt):
+def test_mxfp4_gemv_within_bound_of_exact_dot_product(rows, cols, xt):
+    """y (fp32) against the exact dot product of the decoded weights and x
+    (the oracle's definition), within the stated bound; bf16 and fp16 y are
+    the fp32 result rounded to nearest even."""
     say(f"case gemv rows={rows} cols={cols} x={xt}")
     r = np.random.default_rng(rows * 131 + cols)
     w = mixed(rows * cols, seed=rows + cols, dt="fp32")
     p = oracle.quantize_pack(oracle.MXFP4, w, dtype=oracle.DT_FP32)
     x = datagen.narrow((r.standard_normal(cols) * np.exp(r.uniform(-3, 3, cols))).astype(np.float32), xt)
-    for yt in DTYPES:
-        ref = oracle.mxfp4_gemv(p, rows, cols, x, x_dtype=ORACLE_DT[xt], y_dtype=ORACLE_DT[yt])
-        got = rca.mxfp4_gemv(torch.from_numpy(p).to(DEV), rows, cols, to_dev(x, xt), out_dtype=TORCH_DT[yt]).cpu()
-        g = got.view(torch.int16).numpy().view(np.uint16) if yt == "bf16" else got.numpy()
-        assert_same(g, ref, f"gemv y={yt}")
+    exact, mag = oracle.mxfp4_gemv(p, rows, cols, x, x_dtype=ORACLE_DT[xt])
+    pd, xd = torch.from_numpy(p).to(DEV), to_dev(x, xt)
+    y32 = rca.mxfp4_gemv(pd, rows, cols, xd, out_dtype=torch.float32).cpu().numpy()
+    gemv_bound(y32, exact, mag, cols, f"gemv rows={rows} cols={cols} x={xt}")
+    yb = rca.mxfp4_gemv(pd, rows, cols, xd, out_dtype=torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert_same(yb, oracle.f32_to_bf16_bits(y32), "gemv bf16 y = RN(fp32 y)")
+    yh = rca.mxfp4_gemv(pd, rows, cols, xd, out_dtype=torch.float16).cpu().numpy().view(np.uint16)
+    with np.errstate(over="ignore"):
+        assert_same(yh, oracle.f32_to_f16_bits(y32), "gemv fp16 y = RN(fp32 y)")
 
 
-def test_mxfp4_gemv_weight_4096x4096_sampled_rows():
-    """The 4096 x 4096 bf16 weight recipe, all rows on the GPU; every 37th row
-    and the last against the oracle."""
+def test_mxfp4_gemv_weight_4096x4096_all_rows_within_bound():
+    """The 4096 x 4096 bf16 weight recipe packed on the GPU, bf16 x: every
+    row against the exact dot product, within the bound."""
     rows = cols = 4096
     wbits = datagen.bf16_weight_4096x4096()
     p = rca.quantize_pack(to_dev(wbits, "bf16"), rca.MXFP4)
+    assert np.array_equal(host_u8(p), oracle.quantize_pack_parallel(oracle.MXFP4, wbits, dtype=oracle.DT_BF16))
     x = datagen.narrow(np.random.default_rng(5).standard_normal(cols).astype(np.float32), "bf16")
     y = rca.mxfp4_gemv(p, rows, cols, to_dev(x, "bf16")).cpu().numpy()
-    ph = host_u8(p)
-    pick = list(range(0, rows, 37)) + [rows - 1]
-    tb = oracle.tile_bytes(oracle.MXFP4)
-    sub = np.concatenate([ph[2 * r * tb:(2 * r + 2) * tb] for r in pick])
-    ref = oracle.mxfp4_gemv(sub, len(pick), cols, x, x_dtype=oracle.DT_BF16)
-    assert_same(y[pick], ref, "gemv sampled rows")
+    exact, mag = oracle.mxfp4_gemv(host_u8(p), rows, cols, x, x_dtype=oracle.DT_BF16)
+    gemv_bound(y, exact, mag, cols, "gemv 4096x4096 recipe")
+
+
+@pytest.mark.parametrize("cols", [2048, 6144])
+def test_mxfp4_gemv_exact_sums_and_one_hot(cols):
+    """Order-free exact cases: dyadic weights (block maximum 6, so every E8M0
+    exponent is 0) with integer x make every partial sum exact, so y equals
+    the exact sum bit for bit; a one-hot x returns the decoded weight column."""
+    rows = 70
+    r = np.random.default_rng(cols)
+    idx = r.integers(0, 8, rows * cols)
+    w = (np.array([0, .5, 1, 1.5, 2, 3, 4, 6])[idx] * r.choice([-1, 1], rows * cols)).astype(np.float32)
+    w[::32] = 6.0
+    p = oracle.quantize_pack(oracle.MXFP4, w)
+    pd = torch.from_numpy(p).to(DEV)
+    x = r.integers(-50, 51, cols).astype(np.float32)
+    y = rca.mxfp4_gemv(pd, rows, cols, to_dev(x, "fp32")).cpu().numpy()
+    exact, _ = oracle.mxfp4_gemv(p, rows, cols, x)
+    assert np.array_equal(y.astype(np.float64), exact)
+    wd = oracle.unpack_dequant(oracle.MXFP4, p, rows * cols).reshape(rows, cols)
+    for j in (0, 33, cols - 1):
+        e = np.zeros(cols, dtype=np.float32)
+        e[j] = 1.0
+        yj = rca.mxfp4_gemv(pd, rows, cols, to_dev(e, "fp32")).cpu().numpy()
+        assert np.array_equal(yj, wd[:, j])
 
 
 # ---------------------------------------------------------- beyond 4 GiB ----
