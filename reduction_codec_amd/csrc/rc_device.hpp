@@ -408,15 +408,19 @@ __device__ __forceinline__ uint32_t int3_clamp_word(uint32_t w)
 // E8M0 scales (P2): the multiplier 2^-e is a power of two, so the
 // conversion's own scale operand 2^(e+1) divides exactly and no multiply is
 // needed (e <= 126 for finite data, so the operand is finite).
-template <int H, bool P2>
+// With P = 1 the values come in halved (sums held at 2^-1 of their value),
+// so x / (2 s) is formed with r and r_lo themselves.
+template <int H, bool P2, int P = 0>
 __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const EncScale (&sc)[H])
 {
+    static_assert(P == 0 || (P == 1 && !P2), "pre-scaled values only with FP16 scales");
+    constexpr float k = P == 1 ? 1.0f : 0.5f;
     float r2[H], l2[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) {
         r2[h] = P2 ? __builtin_ldexpf(2.0f, (int)sc[h].bits - 127)   // 2^(e+1), the operand
-                   : 0.5f * sc[h].m;                                  // r/2, exact
-        l2[h] = 0.5f * sc[h].m_lo;                                    // r_lo/2, exact
+                   : k * sc[h].m;                                     // r/2 (or r), exact
+        l2[h] = k * sc[h].m_lo;                                       // r_lo/2 (or r_lo), exact
     }
     uint32_t N[4];
 #pragma unroll
@@ -451,7 +455,9 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
 }
 
 // acc[e] (+)= q_e * S for the 32 elements: E2M1 decode of the nibble (q/2)
-// times dm = 2S (exact products, one rounding per add).
+// times dm = 2S (exact products, one rounding per add); with sums held at
+// half their value, dm = S.  The first term is an fma with a -0 addend,
+// which is the product itself, signed zeros included.
 template <bool FIRST, int H>
 __device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32_t h, const float (&dm)[H],
                                                 float (&acc)[32])
@@ -463,7 +469,10 @@ __device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32
         for (int b = 0; b < 4; ++b) {
             const float m = dm[H == 2 ? b / 2 : 0];
             const f2 c = fp4_dec(Ng, 1.0f, b);
-            if (FIRST) { acc[8 * b + g] = c.x * m; acc[8 * b + 4 + g] = c.y * m; }
+            if (FIRST) {
+                acc[8 * b + g] = __builtin_fmaf(c.x, m, -0.0f);
+                acc[8 * b + 4 + g] = __builtin_fmaf(c.y, m, -0.0f);
+            }
             else {
                 acc[8 * b + g] = __builtin_fmaf(c.x, m, acc[8 * b + g]);
                 acc[8 * b + 4 + g] = __builtin_fmaf(c.y, m, acc[8 * b + 4 + g]);
@@ -488,14 +497,18 @@ __device__ __forceinline__ uint32_t int4_clamp_bytes(uint32_t x)
 // INT4 codes: E4M3 subnormal bytes of x / s * 2^-9 (RNE), formed as
 // fma(x, r 2^-9, x r_lo 2^-9) (FP16 scale) or x 2^-e 2^-9 (E8M0, m_lo = 0),
 // clamped when a block may exceed 7.
-template <int H>
+// With P = 9 the values come in at 2^-9 of their value (pre-scaled sums), so
+// the multipliers are r and r_lo themselves.
+template <int H, int P = 0>
 __device__ __forceinline__ void int4_encode(const float (&v)[32], const EncScale (&sc)[H], uint32_t (&D)[4])
 {
+    static_assert(P == 0 || P == 9, "INT4 values are pre-scaled by 2^-9 or not at all");
+    constexpr float k = P == 9 ? 1.0f : 0x1p-9f;
     float r9[H], l9[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-        r9[h] = sc[h].m * 0x1p-9f;                                       // exact
-        l9[h] = sc[h].m_lo * 0x1p-9f;                                    // exact (>= 2^-50 or 0)
+        r9[h] = sc[h].m * k;                                             // exact
+        l9[h] = sc[h].m_lo * k;                                          // exact (>= 2^-50 or 0)
     }
     // word d's even elements 0,2,4,6 in the bytes of xe[d], odd 1,3,5,7 in xo[d]
     uint32_t xe[4], xo[4];
@@ -545,7 +558,7 @@ __device__ __forceinline__ void int4_accumulate(const uint32_t (&D)[4], float cs
         const float c[8] = {e01.x, o01.x, e01.y, o01.y, e23.x, o23.x, e23.y, o23.y};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (FIRST) acc[8 * d + j] = c[j] * m;
+            if (FIRST) acc[8 * d + j] = __builtin_fmaf(c[j], m, -0.0f);   // the product, signed zeros kept
             else acc[8 * d + j] = __builtin_fmaf(c[j], m, acc[8 * d + j]);
         }
     }
@@ -728,14 +741,16 @@ __device__ __forceinline__ float e8m0_mult(uint32_t b)
 
 // Decode multiplier of one block from its stored scale bits: what the
 // format's code value (as the conversion instructions return it) is
-// multiplied by.
-template <int FMT, int SC>
+// multiplied by.  P: the sums are held at 2^-P of their value (INT with FP16
+// scales in the reduce: P = 1 for INT3, 9 for INT4, where the multiplier is
+// then the fp16 scale itself).
+template <int FMT, int SC, int P = 0>
 __device__ __forceinline__ float dec_mult(uint32_t bits)
 {
     if constexpr (SC == kS16) {
         const float s = __half2float(__ushort_as_half((unsigned short)bits));
-        if constexpr (FMT == 2) return 2.0f * s;          // E2M1 value q/2
-        else if constexpr (FMT == 1) return 512.0f * s;   // E4M3 subnormal q 2^-9
+        if constexpr (FMT == 2) return P == 1 ? s : 2.0f * s;       // E2M1 value q/2
+        else if constexpr (FMT == 1) return P == 9 ? s : 512.0f * s; // E4M3 subnormal q 2^-9
         else return s;
     } else if constexpr (SC == kS32) {
         return __uint_as_float(bits);

@@ -18,6 +18,12 @@
 #ifndef RC_GROUPS_PER_CU
 #define RC_GROUPS_PER_CU 256                       // grid cap, four-wave workgroups per CU
 #endif
+#ifndef RC_REDUCE_GROUPS_PER_CU
+#define RC_REDUCE_GROUPS_PER_CU RC_GROUPS_PER_CU   // reduce grid cap, in four-wave-group units per CU
+#endif
+#ifndef RC_QUANT_GROUPS_PER_CU
+#define RC_QUANT_GROUPS_PER_CU RC_GROUPS_PER_CU    // quantize grid cap, four-wave groups per CU
+#endif
 #ifndef RC_REDUCE_WAVES
 #define RC_REDUCE_WAVES 8                          // reduce occupancy target (waves per SIMD), INT / MX
 #endif
@@ -165,14 +171,25 @@ __device__ __forceinline__ LaneBlock<FMT, SC, BL> load_lane_block(Rsrc r, uint32
     return b;
 }
 
-// acc (+)= decoded values of the lane's 32 elements.
-template <int FMT, int SC, int BL, bool FIRST>
+// Exponent P at which the reduce holds its FP32 sums: value * 2^-P.  INT
+// codes with FP16 scales decode as q/2 (INT3) or q 2^-9 (INT4); keeping the
+// sums at that scale makes the decode multiplier the fp16 scale itself and
+// the requantize multiplier the reciprocal itself.  Exact: every sum is a
+// multiple of at least 2^-34 (codes times fp16 scales >= 2^-24, then 2^-9),
+// far above the binary32 subnormal range, so the scaling commutes with every
+// rounding.
+template <int FMT, int SC> struct SumScale {
+    static constexpr int v = SC == kS16 ? (FMT == kInt3 ? 1 : (FMT == kInt4 ? 9 : 0)) : 0;
+};
+
+// acc (+)= decoded values of the lane's 32 elements (times 2^-P).
+template <int FMT, int SC, int BL, bool FIRST, int P = 0>
 __device__ __forceinline__ void accumulate(const LaneBlock<FMT, SC, BL>& b, float (&acc)[32])
 {
     constexpr int H = Halves<BL>::v;
     float dm[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) dm[h] = dec_mult<FMT, SC>(b.sbits[h]);
+    for (int h = 0; h < H; ++h) dm[h] = dec_mult<FMT, SC, P>(b.sbits[h]);
     if constexpr (FMT == kInt3) {
         int3_accumulate<FIRST, H>(b.c.w0, b.c.w1, b.c.h, dm, acc);
     } else if constexpr (FMT == kInt4) {
@@ -186,9 +203,9 @@ __device__ __forceinline__ void accumulate(const LaneBlock<FMT, SC, BL>& b, floa
     }
 }
 
-// Quantize the lane's 32 values into its code words and scale bits (in
-// registers).
-template <int FMT, int SC, int BL>
+// Quantize the lane's 32 values (held at 2^-P of their value) into its code
+// words and scale bits (in registers).
+template <int FMT, int SC, int BL, int P = 0>
 __device__ __forceinline__ LaneBlock<FMT, SC, BL> encode_lane(const float (&v)[32])
 {
     constexpr int H = Halves<BL>::v;
@@ -196,15 +213,15 @@ __device__ __forceinline__ LaneBlock<FMT, SC, BL> encode_lane(const float (&v)[3
     lane_absmax<BL>(v, a);
     EncScale sc[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) sc[h] = enc_scale<FMT, SC>(a[h]);
+    for (int h = 0; h < H; ++h) sc[h] = enc_scale<FMT, SC>(P ? a[h] * (float)(1u << P) : a[h]);   // exact
     LaneBlock<FMT, SC, BL> b;
 #pragma unroll
     for (int h = 0; h < H; ++h) b.sbits[h] = sc[h].bits;
     if constexpr (FMT == kInt3) {
-        const Int3Words w = int3_encode<H, SC == kSE8>(v, sc);
+        const Int3Words w = int3_encode<H, SC == kSE8, P>(v, sc);
         b.c.w0 = w.w0; b.c.w1 = w.w1; b.c.h = w.h;
     } else if constexpr (FMT == kInt4) {
-        int4_encode<H>(v, sc, b.c.d);
+        int4_encode<H, P>(v, sc, b.c.d);
     } else if constexpr (FMT == kFp8 || FMT == kBf8) {
         fp8_encode<FMT, SC, H>(v, sc, b.c.d);
     } else {
@@ -244,10 +261,10 @@ __device__ __forceinline__ void store_lane_block(const LaneBlock<FMT, SC, BL>& b
     }
 }
 
-template <int FMT, int SC, int BL>
+template <int FMT, int SC, int BL, int P = 0>
 __device__ __forceinline__ void encode_store_buf(const float (&v)[32], Rsrc r, uint32_t lane)
 {
-    store_lane_block<FMT, SC, BL>(encode_lane<FMT, SC, BL>(v), r, lane);
+    store_lane_block<FMT, SC, BL>(encode_lane<FMT, SC, BL, P>(v), r, lane);
 }
 
 __device__ __forceinline__ void wave_lds_sync()
@@ -265,11 +282,12 @@ __device__ __forceinline__ void tail_zero(float (&acc)[32], size_t base, size_t 
         if ((size_t)e >= valid) acc[e] = 0.0f;
 }
 
+template <int P>
 __device__ __forceinline__ void store_sums_tail(float* __restrict__ sum_out, size_t base, size_t n, const float (&acc)[32])
 {
 #pragma unroll
     for (int e = 0; e < 32; ++e)
-        if (base + e < n) sum_out[base + e] = acc[e];
+        if (base + e < n) sum_out[base + e] = acc[e] * (float)(1u << P);
 }
 
 // ------------------------------------------------------------ kernels ----
@@ -450,6 +468,7 @@ template <int FMT, int SC, int BL, int K>
 __device__ __forceinline__ void reduce_tile(const StreamPtrs& ins, int k, size_t tile, uint32_t lane, float (&acc)[32])
 {
     constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
+    constexpr int P = SumScale<FMT, SC>::v;
     if constexpr (ReduceRoll<FMT, SC>::v && K > 2) {
         // rolling: stream j is loaded as soon as stream j - 2 is decoded, so
         // two streams' codes are in flight at any time
@@ -460,8 +479,8 @@ __device__ __forceinline__ void reduce_tile(const StreamPtrs& ins, int k, size_t
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            if (j == 0) accumulate<FMT, SC, BL, true>(c[0], acc);
-            else accumulate<FMT, SC, BL, false>(c[j], acc);
+            if (j == 0) accumulate<FMT, SC, BL, true, P>(c[0], acc);
+            else accumulate<FMT, SC, BL, false, P>(c[j], acc);
             if (j + 2 < K) {
                 __builtin_amdgcn_sched_barrier(0);
                 c[j + 2] = load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j + 2], tile * TB, TB), lane);
@@ -479,34 +498,37 @@ __device__ __forceinline__ void reduce_tile(const StreamPtrs& ins, int k, size_t
 #pragma unroll
             for (int j = 0; j < B; ++j) {
                 if (k0 + j >= K) break;
-                if (k0 + j == 0) accumulate<FMT, SC, BL, true>(c[j], acc);
-                else accumulate<FMT, SC, BL, false>(c[j], acc);
+                if (k0 + j == 0) accumulate<FMT, SC, BL, true, P>(c[j], acc);
+                else accumulate<FMT, SC, BL, false, P>(c[j], acc);
             }
             // keep the next batch's loads below this batch's arithmetic (bounds
             // the registers held by codes in flight)
             if (RC_REDUCE_SCHED_BARRIER && k0 + B < K) __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        accumulate<FMT, SC, BL, true>(load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[0], tile * TB, TB), lane), acc);
+        accumulate<FMT, SC, BL, true, P>(load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[0], tile * TB, TB), lane), acc);
         int j = 1;
         for (; j + 1 < k; j += 2) {
             const LaneBlock<FMT, SC, BL> c0 = load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j], tile * TB, TB), lane);
             const LaneBlock<FMT, SC, BL> c1 = load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j + 1], tile * TB, TB), lane);
-            accumulate<FMT, SC, BL, false>(c0, acc);
-            accumulate<FMT, SC, BL, false>(c1, acc);
+            accumulate<FMT, SC, BL, false, P>(c0, acc);
+            accumulate<FMT, SC, BL, false, P>(c1, acc);
         }
         if (j < k)
-            accumulate<FMT, SC, BL, false>(load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j], tile * TB, TB), lane), acc);
+            accumulate<FMT, SC, BL, false, P>(load_lane_block<FMT, SC, BL>(span_rsrc(ins.p[j], tile * TB, TB), lane), acc);
     }
 }
 
+// The FP32 sums (held at 2^-P of their value) written out at their value.
+template <int P>
 __device__ __forceinline__ void store_sums(float* __restrict__ sum_out, size_t tile, uint32_t lane, const float (&acc)[32])
 {
     const Rsrc r = span_rsrc(sum_out, tile * (kTile * 4), kTile * 4);
+    constexpr float k = (float)(1u << P);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128((u32x4){__float_as_uint(acc[4 * i]), __float_as_uint(acc[4 * i + 1]),
-                                                       __float_as_uint(acc[4 * i + 2]), __float_as_uint(acc[4 * i + 3])},
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){__float_as_uint(acc[4 * i] * k), __float_as_uint(acc[4 * i + 1] * k),
+                                                       __float_as_uint(acc[4 * i + 2] * k), __float_as_uint(acc[4 * i + 3] * k)},
                                                r, lane * 128u + 16u * i, 0, kNT);
 }
 
@@ -521,6 +543,7 @@ void reduce_kernel(StreamPtrs ins, int k, size_t n, uint8_t* __restrict__ out, f
                    size_t tiles)
 {
     constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
+    constexpr int P = SumScale<FMT, SC>::v;
     const TileWalk tw = tile_walk<ReduceGroupWaves<FMT, SC, BL>::v>();
     const uint32_t lane = (uint32_t)tw.lane;
     const size_t full = n / kTile;
@@ -528,14 +551,14 @@ void reduce_kernel(StreamPtrs ins, int k, size_t n, uint8_t* __restrict__ out, f
         for (size_t tile = tw.first; tile < full; tile += tw.stride) {
             float acc[32];
             reduce_tile<FMT, SC, BL, K>(ins, k, tile, lane, acc);
-            store_sums(sum_out, tile, lane, acc);
-            encode_store_buf<FMT, SC, BL>(acc, span_rsrc(out, tile * TB, TB), lane);
+            store_sums<P>(sum_out, tile, lane, acc);
+            encode_store_buf<FMT, SC, BL, P>(acc, span_rsrc(out, tile * TB, TB), lane);
         }
     } else {
         for (size_t tile = tw.first; tile < full; tile += tw.stride) {
             float acc[32];
             reduce_tile<FMT, SC, BL, K>(ins, k, tile, lane, acc);
-            encode_store_buf<FMT, SC, BL>(acc, span_rsrc(out, tile * TB, TB), lane);
+            encode_store_buf<FMT, SC, BL, P>(acc, span_rsrc(out, tile * TB, TB), lane);
         }
     }
     if (full != tiles && full % tw.stride == tw.first) {
@@ -543,8 +566,8 @@ void reduce_kernel(StreamPtrs ins, int k, size_t n, uint8_t* __restrict__ out, f
         reduce_tile<FMT, SC, BL, K>(ins, k, full, lane, acc);
         const size_t base = full * kTile + (size_t)lane * 32;
         tail_zero(acc, base, n);                   // positions >= n are +0
-        if (sum_out) store_sums_tail(sum_out, base, n, acc);
-        encode_store_buf<FMT, SC, BL>(acc, span_rsrc(out, full * TB, TB), lane);
+        if (sum_out) store_sums_tail<P>(sum_out, base, n, acc);
+        encode_store_buf<FMT, SC, BL, P>(acc, span_rsrc(out, full * TB, TB), lane);
     }
 }
 
@@ -867,12 +890,12 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
 // tile per wave up to 4 * RC_GROUPS_PER_CU waves per compute unit (1 GiB of
 // bf16 input on 256 CUs; measured faster there than a 4x smaller grid
 // walking 4 tiles per wave); beyond that each wave walks several tiles.
-static inline dim3 tile_grid(size_t tiles, int waves = kWavesPerGroup)
+static inline dim3 tile_grid(size_t tiles, int waves = kWavesPerGroup, int groups_per_cu = RC_GROUPS_PER_CU)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const size_t groups = (tiles + waves - 1) / waves;
-    const size_t cap = (size_t)RC_GROUPS_PER_CU * (size_t)(cus > 0 ? cus : 256) * (size_t)(kWavesPerGroup / waves);
+    const size_t cap = (size_t)groups_per_cu * (size_t)(cus > 0 ? cus : 256) * (size_t)(kWavesPerGroup / waves);
     return dim3((unsigned)(groups < cap ? groups : cap));
 }
 
@@ -882,9 +905,9 @@ hipError_t launch_quantize_t(int dt, const void* in, size_t n, void* out, hipStr
     const size_t tiles = (n + kTile - 1) / kTile;
     uint8_t* o = static_cast<uint8_t*>(out);
     switch (dt) {
-    case kF32: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF32>), tile_grid(tiles), dim3(256), 0, st, in, n, o, tiles); break;
-    case kF16: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF16>), tile_grid(tiles), dim3(256), 0, st, in, n, o, tiles); break;
-    default:   hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kBF16>), tile_grid(tiles), dim3(256), 0, st, in, n, o, tiles); break;
+    case kF32: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF32>), tile_grid(tiles, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
+    case kF16: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF16>), tile_grid(tiles, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
+    default:   hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kBF16>), tile_grid(tiles, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
     }
     return hipGetLastError();
 }
@@ -915,7 +938,7 @@ static hipError_t launch_reduce_k(const StreamPtrs& p, int k, size_t n, void* ou
 {
     const size_t tiles = (n + kTile - 1) / kTile;
     constexpr int W = ReduceGroupWaves<FMT, SC, BL>::v;
-    hipLaunchKernelGGL((reduce_kernel<FMT, SC, BL, K>), tile_grid(tiles, W), dim3(64 * W), 0, st, p, k, n,
+    hipLaunchKernelGGL((reduce_kernel<FMT, SC, BL, K>), tile_grid(tiles, W, RC_REDUCE_GROUPS_PER_CU), dim3(64 * W), 0, st, p, k, n,
                        static_cast<uint8_t*>(out), sum, tiles);
     return hipGetLastError();
 }
