@@ -57,6 +57,12 @@
 #ifndef RC_RT_UNROLL_COMMON
 #define RC_RT_UNROLL_COMMON 1                      // variants: 2, 4, 8 streams unrolled too
 #endif
+#ifndef RC_GEMV_ROWS
+#define RC_GEMV_ROWS 2                             // rows per wave of the GEMV
+#endif
+#ifndef RC_GEMV_DOT2
+#define RC_GEMV_DOT2 1                             // bf16 x: v_dot2_f32_bf16 on bf16 weight pairs
+#endif
 #ifndef RC_UNPACK_LDS
 #define RC_UNPACK_LDS 1                            // unpack output regrouped through LDS
 #endif
@@ -771,12 +777,14 @@ void allreduce_kernel(StreamPtrs msgs, int k, size_t n, void* __restrict__ out, 
 // ------------------------------------------------------------ MXFP4 GEMV ----
 //
 // y = W x on an MXFP4-packed row-major matrix (row r = tiles r*T .. r*T+T-1).
-// The summation order is the definition: lane l of a row owns block 64j + l
-// of tile j; a block term is an fma chain over its 32 elements in order from
-// +0, times 2^e (one rounding, v_ldexp); the lane adds its block terms in
-// tile order; then an xor butterfly over the 64 lanes (offsets 32..1); lane 0
-// writes y[r].  One wave per row, R rows per wave iteration; with T <= 2 the
-// lane's x values live in registers across rows.
+// The result is specified by a rounding bound, not by an order; the order
+// used here: lane l of a wave holds block l of every tile of R rows (the
+// same 32 columns for all R rows, so the lane's x values are loaded once and
+// used R times); a block term is four interleaved fma chains of 8 elements,
+// added pairwise, times 2^e (one ldexp); the lane adds its block terms over
+// the tiles; then the 64 lane sums of a row are added within quads and rows
+// of 16 lanes (DPP) and the four row sums read out (readlane) and added.
+// Every term passes through at most 8 + 2 + T + 6 binary32 roundings.
 
 // The lane's 32 x values of tile j (elements j*2048 + 32 lane .. + 31).
 template <int XT>
@@ -797,30 +805,99 @@ __device__ __forceinline__ void load_x32(Rsrc xr, int j, uint32_t lane, float (&
     }
 }
 
-// Block term 2^e * (fma chain over the lane's 32 elements of one tile).
-__device__ __forceinline__ float gemv_block_term(Rsrc wt, uint32_t lane, const float (&xv)[32])
+// The lane's block of one tile: 32 E2M1 codes and the E8M0 byte.
+struct GemvBlock { uint32_t d[4]; uint32_t sb; };
+
+__device__ __forceinline__ GemvBlock gemv_load(Rsrc wt, uint32_t lane)
 {
+    GemvBlock b;
     const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(wt, lane * 16u, 0, kNT);
-    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(wt, 1024u + lane, 0, kNT);
-    const uint32_t d[4] = {c.x, c.y, c.z, c.w};
-    float p = 0.0f;
+    b.d[0] = c.x; b.d[1] = c.y; b.d[2] = c.z; b.d[3] = c.w;
+    b.sb = __builtin_amdgcn_raw_buffer_load_b8(wt, 1024u + lane, 0, kNT);
+    return b;
+}
+
+// Block term 2^e * sum over the block's 32 elements of code * x: four
+// interleaved chains (elements 8c + 2b and 8c + 2b + 1 of word c go to chains
+// 2(c%2) and 2(c%2) + 1), added pairwise.
+__device__ __forceinline__ float gemv_block_term(const GemvBlock& b, const float (&xv)[32])
+{
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const f2 v = fp4_dec(d[w], 1.0f, b);            // elements 8w+2b, 8w+2b+1
-            p = __builtin_fmaf(v.x, xv[8 * w + 2 * b], p);
-            p = __builtin_fmaf(v.y, xv[8 * w + 2 * b + 1], p);
+        for (int k = 0; k < 4; ++k) {
+            const f2 v = fp4_dec(b.d[w], 1.0f, k);            // elements 8w+2k, 8w+2k+1
+            p[2 * (w & 1)] = __builtin_fmaf(v.x, xv[8 * w + 2 * k], p[2 * (w & 1)]);
+            p[2 * (w & 1) + 1] = __builtin_fmaf(v.y, xv[8 * w + 2 * k + 1], p[2 * (w & 1) + 1]);
         }
     }
-    return (sb == 255u) ? __builtin_nanf("") : __builtin_ldexpf(p, (int)sb - 127);
+    const float t = (p[0] + p[1]) + (p[2] + p[3]);
+    return (b.sb == 255u) ? __builtin_nanf("") : __builtin_ldexpf(t, (int)b.sb - 127);
 }
 
-__device__ __forceinline__ float butterfly_sum(float v)
+// bf16 x: the lane's 32 x values of tile j kept as 16 packed bf16 pairs, and
+// the block term from bf16 pairs of decoded weights (E2M1 values are exact in
+// bf16) with v_dot2_f32_bf16: two exact products and the running sum per
+// instruction, four interleaved chains of four, added pairwise, times 2^e.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void load_x32_bf16(Rsrc xr, int j, uint32_t lane, uint32_t (&xw)[16])
 {
+    const uint32_t off = ((uint32_t)j * kTile + lane * 32u) * 2u;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off, 64);
-    return v;
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * i, 0, 0);
+        xw[4 * i] = u.x; xw[4 * i + 1] = u.y; xw[4 * i + 2] = u.z; xw[4 * i + 3] = u.w;
+    }
+}
+
+__device__ __forceinline__ bf16x2 fp4_dec_bf16(uint32_t w, int sel)
+{
+    switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+    }
+}
+
+__device__ __forceinline__ float gemv_block_term_bf16(const GemvBlock& b, const uint32_t (&xw)[16])
+{
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = 2 * (w & 1) + (k & 1);
+            p[c] = __builtin_amdgcn_fdot2_f32_bf16(fp4_dec_bf16(b.d[w], k), __builtin_bit_cast(bf16x2, xw[4 * w + k]),
+                                                    p[c], false);
+        }
+    }
+    const float t = (p[0] + p[1]) + (p[2] + p[3]);
+    return (b.sb == 255u) ? __builtin_nanf("") : __builtin_ldexpf(t, (int)b.sb - 127);
+}
+
+// v + the value of the lane named by the DPP control (a quad permutation or
+// a rotation within a row of 16 lanes), all lanes active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The sum of v over the 64 lanes of the wave, as a wave-uniform value.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = dpp_add<0xB1>(v);        // quad_perm [1,0,3,2]: pairs
+    v = dpp_add<0x4E>(v);        // quad_perm [2,3,0,1]: quads
+    v = dpp_add<0x124>(v);       // row_ror:4  : two quads
+    v = dpp_add<0x128>(v);       // row_ror:8  : the row of 16
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
 }
 
 template <int YT>
@@ -831,8 +908,10 @@ __device__ __forceinline__ void store_y(void* y, size_t r, float v)
     else static_cast<uint16_t*>(y)[r] = (uint16_t)f16_bits(v);
 }
 
-// TC = T when T <= 2 (x in registers), 0 for any T (x reloaded per tile).
-template <int XT, int YT, int TC>
+// One wave per R consecutive rows (a group of four waves per 4R rows).  TC =
+// T when T <= 2: x and all R x T weight blocks are loaded before any
+// arithmetic; TC = 0: any T, tile by tile.
+template <int XT, int YT, int TC, int R>
 __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restrict__ w, size_t rows, int T,
                                                          const void* __restrict__ x, void* __restrict__ y)
 {
@@ -841,45 +920,67 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
     const TileWalk tw = tile_walk();
     const uint32_t lane = (uint32_t)tw.lane;
     const Rsrc xr = span_rsrc(x, 0, (uint32_t)T * kTile * ES);
-    if constexpr (TC > 0) {
-        float xv[TC][32];
+    for (size_t r0 = tw.first * R; r0 < rows; r0 += tw.stride * R) {
+        float L[R];
+        if constexpr (TC > 0 && XT == kBF16 && RC_GEMV_DOT2) {
+            uint32_t xw[TC][16];
+            GemvBlock b[R][TC];
 #pragma unroll
-        for (int j = 0; j < TC; ++j) load_x32<XT>(xr, j, lane, xv[j]);
-        size_t r = tw.first;
-        for (; r + tw.stride < rows; r += 2 * tw.stride) {        // two rows at a time
-            float L0 = 0.0f, L1 = 0.0f;
+            for (int i = 0; i < R; ++i)
 #pragma unroll
-            for (int j = 0; j < TC; ++j) {
-                const float t0 = gemv_block_term(span_rsrc(w, (r * TC + j) * TB, TB), lane, xv[j]);
-                const float t1 = gemv_block_term(span_rsrc(w, ((r + tw.stride) * TC + j) * TB, TB), lane, xv[j]);
-                L0 = (j == 0) ? t0 : L0 + t0;
-                L1 = (j == 0) ? t1 : L1 + t1;
+                for (int j = 0; j < TC; ++j)
+                    if (r0 + i < rows) b[i][j] = gemv_load(span_rsrc(w, ((r0 + i) * TC + j) * TB, TB), lane);
+#pragma unroll
+            for (int j = 0; j < TC; ++j) load_x32_bf16(xr, j, lane, xw[j]);
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                L[i] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < TC; ++j) {
+                    const float t = (r0 + i < rows) ? gemv_block_term_bf16(b[i][j], xw[j]) : 0.0f;
+                    L[i] = (j == 0) ? t : L[i] + t;
+                }
             }
-            L0 = butterfly_sum(L0);
-            L1 = butterfly_sum(L1);
-            if (lane == 0) { store_y<YT>(y, r, L0); store_y<YT>(y, r + tw.stride, L1); }
-        }
-        if (r < rows) {
-            float L = 0.0f;
+        } else if constexpr (TC > 0) {
+            float xv[TC][32];
+            GemvBlock b[R][TC];
 #pragma unroll
-            for (int j = 0; j < TC; ++j) {
-                const float t = gemv_block_term(span_rsrc(w, (r * TC + j) * TB, TB), lane, xv[j]);
-                L = (j == 0) ? t : L + t;
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int j = 0; j < TC; ++j)
+                    if (r0 + i < rows) b[i][j] = gemv_load(span_rsrc(w, ((r0 + i) * TC + j) * TB, TB), lane);
+#pragma unroll
+            for (int j = 0; j < TC; ++j) load_x32<XT>(xr, j, lane, xv[j]);
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                L[i] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < TC; ++j) {
+                    const float t = (r0 + i < rows) ? gemv_block_term(b[i][j], xv[j]) : 0.0f;
+                    L[i] = (j == 0) ? t : L[i] + t;
+                }
             }
-            L = butterfly_sum(L);
-            if (lane == 0) store_y<YT>(y, r, L);
-        }
-    } else {
-        for (size_t r = tw.first; r < rows; r += tw.stride) {
-            float L = 0.0f;
+        } else {
+#pragma unroll
+            for (int i = 0; i < R; ++i) L[i] = 0.0f;
             for (int j = 0; j < T; ++j) {
                 float xv[32];
+                GemvBlock b[R];
+#pragma unroll
+                for (int i = 0; i < R; ++i)
+                    if (r0 + i < rows) b[i] = gemv_load(span_rsrc(w, ((r0 + i) * (size_t)T + j) * TB, TB), lane);
                 load_x32<XT>(xr, j, lane, xv);
-                const float t = gemv_block_term(span_rsrc(w, (r * (size_t)T + j) * TB, TB), lane, xv);
-                L = (j == 0) ? t : L + t;
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const float t = (r0 + i < rows) ? gemv_block_term(b[i], xv) : 0.0f;
+                    L[i] = (j == 0) ? t : L[i] + t;
+                }
             }
-            L = butterfly_sum(L);
-            if (lane == 0) store_y<YT>(y, r, L);
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float s = wave_sum(L[i]);
+            if (lane == 0 && r0 + i < rows) store_y<YT>(y, r0 + i, s);
         }
     }
 }
@@ -984,19 +1085,21 @@ hipError_t launch_allreduce_t(int dt, const StreamPtrs& msgs, int k, size_t n, i
     return hipGetLastError();
 }
 
+
 template <int XT, int YT>
 static hipError_t launch_gemv_xy(const void* w, size_t rows, int T, const void* x, void* y, hipStream_t st)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    // one row per wave, at most 16 four-wave workgroups per CU (rows loop beyond)
-    size_t groups = (rows + kWavesPerGroup - 1) / kWavesPerGroup;
+    constexpr int R = RC_GEMV_ROWS;
+    // R rows per wave, four waves per group, at most 16 groups per CU (rows loop beyond)
+    size_t groups = (rows + 4 * R - 1) / (4 * R);
     const size_t cap = (size_t)16 * (size_t)(cus > 0 ? cus : 256);
     if (groups > cap) groups = cap;
     const uint8_t* wp = static_cast<const uint8_t*>(w);
-    if (T == 1) hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 1>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
-    else if (T == 2) hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 2>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
-    else hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 0>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
+    if (T == 1) hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 1, R>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
+    else if (T == 2) hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 2, R>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
+    else hipLaunchKernelGGL((mxfp4_gemv_kernel<XT, YT, 0, R>), dim3((unsigned)groups), dim3(256), 0, st, wp, rows, T, x, y);
     return hipGetLastError();
 }
 

@@ -613,6 +613,37 @@ def test_mxfp4_gemv_weight_4096x4096_all_rows_within_bound():
     gemv_bound(y, exact, mag, cols, "gemv 4096x4096 recipe")
 
 
+@pytest.mark.parametrize("case", ["x_bf16_subnormal", "x_bf16_mixed_magnitudes", "w_tiny_blocks"])
+@pytest.mark.parametrize("xt", DTYPES)
+def test_mxfp4_gemv_edge_magnitudes_within_bound(case, xt):
+    """Inputs at the edges of the number range, every x dtype: x made of
+    subnormal values (bf16 / fp16 / fp32 subnormals), x spanning 2^-60..2^60
+    with zeros and -0, and weight blocks whose E8M0 exponent is near -127; y
+    within the bound of the exact dot product."""
+    rows, cols = 40, 4096
+    say(f"case gemv edge {case} x={xt}")
+    r = np.random.default_rng(hash(case) % 1000)
+    w = r.standard_normal(rows * cols).astype(np.float32)
+    if case == "w_tiny_blocks":
+        w[: rows * cols // 2] *= np.float32(2.0 ** -120)
+    p = oracle.quantize_pack(oracle.MXFP4, w)
+    if case == "x_bf16_subnormal":
+        tiny = {"bf16": 2.0 ** -130, "fp16": 2.0 ** -20, "fp32": 2.0 ** -140}[xt]
+        x = (r.standard_normal(cols) * tiny).astype(np.float32)
+    elif case == "x_bf16_mixed_magnitudes":
+        x = (r.standard_normal(cols) * 2.0 ** r.integers(-60, 60, cols)).astype(np.float32)
+        if xt == "fp16":
+            x = (r.standard_normal(cols) * 2.0 ** r.integers(-20, 12, cols)).astype(np.float32)
+        x[::7] = 0.0
+        x[3::7] = -0.0
+    else:
+        x = (r.standard_normal(cols)).astype(np.float32)
+    x = datagen.narrow(x, xt)
+    exact, mag = oracle.mxfp4_gemv(p, rows, cols, x, x_dtype=ORACLE_DT[xt])
+    y = rca.mxfp4_gemv(torch.from_numpy(p).to(DEV), rows, cols, to_dev(x, xt)).cpu().numpy()
+    gemv_bound(y, exact, mag, cols, f"gemv edge {case} x={xt}")
+
+
 @pytest.mark.parametrize("cols", [2048, 6144])
 def test_mxfp4_gemv_exact_sums_and_one_hot(cols):
     """Order-free exact cases: dyadic weights (block maximum 6, so every E8M0
