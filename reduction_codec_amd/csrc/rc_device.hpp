@@ -292,7 +292,8 @@ __device__ __forceinline__ int e8m0_exponent(float a)
 struct EncScale {
     uint32_t bits;
     float m;
-    float m_lo;      // INT/FP16 only
+    float m_lo;      // INT/FP16: low part of the reciprocal; FP8/FP32: a - s fmax
+                     // (exact: its sign says which way s was rounded)
     bool zero;       // FP16/FP32 scale 0: the block is stored as zeros
     bool clamp;      // codes may exceed the format's largest magnitude
 };
@@ -324,6 +325,7 @@ __device__ __forceinline__ EncScale enc_scale(float a)
             r.zero = !(s >= 0x1p-126f);
             r.bits = r.zero ? 0u : __float_as_uint(s);
             r.m = s;
+            r.m_lo = __builtin_fmaf(-s, (float)Fmt<FMT>::fmax, a);
         } else if constexpr (SC == kS16) {
             const float s32 = fminf(div_by<Fmt<FMT>::fmax>(a), 65504.0f);            // NaN (inf a) -> 65504
             const __half h = __float2half_rn(s32);
@@ -585,22 +587,22 @@ __device__ __forceinline__ f2 f8_dec(uint32_t w, bool hi)
 // Round-to-odd binary32 value of the exact quotient |x| / s, with the sign
 // of x and clamped to FMAX; its round-to-nearest-even conversion to E4M3 or
 // E5M2 equals that of the exact quotient (binary32 carries more than 4 + 2
-// significant bits).  rs is the hardware reciprocal of s (within 1 ulp):
-//   y0 = |x| * rs is within 3 ulp of the quotient q,
-//   y1 = y0 + fma(-y0, s, |x|) * rs is within 1/2 ulp (plus 2^-20 ulp) of q,
-//   and the sign of r = fma(-y1, s, |x|) (zero only when y1 = q) says on
-//   which side of y1 the quotient lies.
+// significant bits).  rs is the hardware reciprocal of s (within 1 ulp) and
+// rl = fma(-s, rs, 1) * rs its low part, so that
+//   y1 = fma(|x|, rs, |x| * rl) lies within 1 ulp of the quotient q, and
+//   r = fma(-y1, s, |x|) is exact, zero only when y1 = q, negative when q
+//   lies below y1: its sign bit steps y1 down to the binary32 value just
+//   below q, and a nonzero r sets the last bit (round to odd).
+// An overflowed y1 = inf gives r = -inf and so the largest finite value.
 // The residuals must not underflow: callers pass s >= 2^-64 (smaller block
 // scales are handled by multiplying x and s by 2^64).
 template <int FMAX, bool CLAMP>
-__device__ __forceinline__ float fp8_ro_quotient(float x, float s, float rs)
+__device__ __forceinline__ float fp8_ro_quotient(float x, float s, float rs, float rl)
 {
     const float ax = fabsf(x);
-    const float y0 = ax * rs;
-    const float y1 = __builtin_fmaf(__builtin_fmaf(-y0, s, ax), rs, y0);
-    const float r = __builtin_fmaf(-y1, s, ax);
-    uint32_t t = __float_as_uint(y1);
-    t = (t - (r < 0.0f ? 1u : 0u)) | (r != 0.0f ? 1u : 0u);
+    const float y1 = __builtin_fmaf(ax, rs, ax * rl);
+    const uint32_t rb = __float_as_uint(__builtin_fmaf(-y1, s, ax));
+    const uint32_t t = (__float_as_uint(y1) - (rb >> 31)) | min(rb, 1u);
     const float yo = CLAMP ? fminf(__uint_as_float(t), (float)FMAX) : __uint_as_float(t);
     return __uint_as_float(__float_as_uint(yo) | (__float_as_uint(x) & 0x80000000u));
 }
@@ -613,26 +615,99 @@ template <int FMT, int H, bool CLAMP>
 __device__ __forceinline__ void fp8_quotient_codes(const float (&v)[32], const float (&sk)[H], float k,
                                                    uint32_t (&d)[8])
 {
-    float rs[H];
+    float rs[H], rl[H];
 #pragma unroll
-    for (int h = 0; h < H; ++h) rs[h] = __builtin_amdgcn_rcpf(sk[h]);
+    for (int h = 0; h < H; ++h) {
+        rs[h] = __builtin_amdgcn_rcpf(sk[h]);
+        rl[h] = __builtin_fmaf(-sk[h], rs[h], 1.0f) * rs[h];
+    }
     constexpr int FM = Fmt<FMT>::fmax;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int h = H == 2 ? i / 4 : 0;
         const float* x = v + 4 * i;
-        const float q0 = fp8_ro_quotient<FM, CLAMP>(x[0] * k, sk[h], rs[h]);
-        const uint32_t w = f8_pair<FMT>(q0, fp8_ro_quotient<FM, CLAMP>(x[1] * k, sk[h], rs[h]),
+        const float q0 = fp8_ro_quotient<FM, CLAMP>(x[0] * k, sk[h], rs[h], rl[h]);
+        const uint32_t w = f8_pair<FMT>(q0, fp8_ro_quotient<FM, CLAMP>(x[1] * k, sk[h], rs[h], rl[h]),
                                         __float_as_uint(q0), false);     // starts from q0's own bits
-        d[i] = f8_pair<FMT>(fp8_ro_quotient<FM, CLAMP>(x[2] * k, sk[h], rs[h]),
-                            fp8_ro_quotient<FM, CLAMP>(x[3] * k, sk[h], rs[h]), w, true);
+        d[i] = f8_pair<FMT>(fp8_ro_quotient<FM, CLAMP>(x[2] * k, sk[h], rs[h], rl[h]),
+                            fp8_ro_quotient<FM, CLAMP>(x[3] * k, sk[h], rs[h], rl[h]), w, true);
     }
 }
 
-// FP8 codes (E4M3 / E5M2): with an FP32 or FP16 scale the exact-quotient
-// rounding above; with an E8M0 scale x * 2^-e is exact, clamped to the
-// format's largest magnitude and converted (RNE).
-template <int FMT, int SC, int H>
+// Codes of x * r (r = the reciprocal rounded down by 2^-21) and of x * R
+// (rounded up by 2^-21), clamped to the largest magnitude when CLAMP.
+// Against the hardware reciprocal's 1 ulp and the roundings of r and of the
+// products, the two products enclose the quotient x / s; the conversion
+// (nearest even, after the clamp) is monotone, so where both give one code
+// that is the code of the quotient.  Where they differ (adjacent codes) the
+// quotient lies within 2^-20 of the midpoint m between them:
+//   - NARROW (x and the block maximum a carry at most 11 significant bits,
+//     as bf16 and fp16 values do): then the quotient is an exact tie of
+//     fmax x = m a (FP32 scale; s = a / fmax rounded, so the quotient lies
+//     above m when s was rounded down, dir = a - s fmax > 0, below when up,
+//     on it when exact) or of x = m s (FP16 scale, dir = 0), because any
+//     other distance from a midpoint is at least 2^-16 relative.  The code
+//     is taken per byte: the upper one, the lower one, or the even one.
+//   - otherwise, where some lane of the wave has such an element in a word
+//     of four codes, the exact sequence recomputes that word (fp32 sums and
+//     messages seldom need it; sums of two streams, often a single decoded
+//     term, do for about one word in eight).
+// Callers pass s >= 2^-64 in every lane.
+template <int FMT, int H, bool CLAMP, bool NARROW>
+__device__ __forceinline__ void fp8_bracket_codes(const float (&v)[32], const float (&s)[H], const float (&dir)[H],
+                                                  uint32_t (&d)[8])
+{
+    constexpr float FM = (float)Fmt<FMT>::fmax;
+    constexpr int FMI = Fmt<FMT>::fmax;
+    float rs[H], rl[H], rlo[H], rhi[H];
+    uint32_t up[H], tie[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        rs[h] = __builtin_amdgcn_rcpf(s[h]);
+        rl[h] = __builtin_fmaf(-s[h], rs[h], 1.0f) * rs[h];
+        rlo[h] = rs[h] * 0x1.fffffp-1f;         // 1 - 2^-21
+        rhi[h] = rs[h] * 0x1.000008p0f;         // 1 + 2^-21
+        up[h] = dir[h] > 0.0f ? 0x01010101u : 0u;
+        tie[h] = dir[h] == 0.0f ? 0x01010101u : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int h = H == 2 ? i / 4 : 0;
+        float a[4], b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[j] = v[4 * i + j] * rlo[h];
+            b[j] = v[4 * i + j] * rhi[h];
+            if constexpr (CLAMP) {
+                a[j] = __builtin_amdgcn_fmed3f(a[j], -FM, FM);
+                b[j] = __builtin_amdgcn_fmed3f(b[j], -FM, FM);
+            }
+        }
+        uint32_t lo = f8_pair<FMT>(a[2], a[3], f8_pair<FMT>(a[0], a[1], __float_as_uint(a[0]), false), true);
+        const uint32_t hi = f8_pair<FMT>(b[2], b[3], f8_pair<FMT>(b[0], b[1], __float_as_uint(b[0]), false), true);
+        if constexpr (NARROW) {
+            // byte k from hi where the lower code is odd (ties) or dir > 0:
+            // selector k + 4 picks hi's byte k, k picks lo's
+            d[i] = __builtin_amdgcn_perm(hi, lo, (((lo & tie[h]) | up[h]) << 2) | 0x03020100u);
+        } else {
+            if (__builtin_amdgcn_ballot_w64(lo != hi) != 0u) {         // wave-uniform
+                const float* x = v + 4 * i;
+                const float q0 = fp8_ro_quotient<FMI, CLAMP>(x[0], s[h], rs[h], rl[h]);
+                lo = f8_pair<FMT>(q0, fp8_ro_quotient<FMI, CLAMP>(x[1], s[h], rs[h], rl[h]), __float_as_uint(q0), false);
+                lo = f8_pair<FMT>(fp8_ro_quotient<FMI, CLAMP>(x[2], s[h], rs[h], rl[h]),
+                                  fp8_ro_quotient<FMI, CLAMP>(x[3], s[h], rs[h], rl[h]), lo, true);
+            }
+            d[i] = lo;
+        }
+    }
+}
+
+// FP8 codes (E4M3 / E5M2): with an FP32 or FP16 scale the code of the exact
+// quotient, from the bracket above or, in a wave where some lane's scale is
+// below 2^-64, from the round-to-odd sequence for every code; with an E8M0
+// scale x * 2^-e is exact, clamped to the format's largest magnitude and
+// converted (RNE).
+template <int FMT, int SC, int H, bool NARROW>
 __device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale (&sc)[H], uint32_t (&d)[8])
 {
     constexpr float FM = (float)Fmt<FMT>::fmax;
@@ -646,11 +721,12 @@ __device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale 
             d[i] = f8_pair<FMT>(y[2], y[3], f8_pair<FMT>(y[0], y[1], __float_as_uint(y[0]), false), true);
         }
     } else {
-        float s[H];
+        float s[H], dir[H];
         bool tiny = false;
 #pragma unroll
         for (int h = 0; h < H; ++h) {
             s[h] = sc[h].zero ? 1.0f : sc[h].m;
+            dir[h] = sc[h].m_lo;
             if constexpr (SC == kS32) tiny = tiny || (s[h] < 0x1p-64f);
         }
         // FP32 scale: s = RN32(absmax / fmax) is normal or the block is zero,
@@ -659,13 +735,17 @@ __device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale 
         // value stays below the first value that would overflow.  FP16
         // scales (subnormal or clamped at 65504) need the clamp.
         constexpr bool CL = SC != kS32;
-        if (!tiny) {
-            fp8_quotient_codes<FMT, H, CL>(v, s, 1.0f, d);
-        } else {                              // tiny scale: x * 2^64 and s * 2^64 are exact
-            float sk[H];
+        if (__builtin_amdgcn_ballot_w64(tiny) == 0u) {                  // wave-uniform
+            fp8_bracket_codes<FMT, H, CL, NARROW>(v, s, dir, d);
+        } else {                              // some scale below 2^-64: the exact sequence
+            if (!tiny) {
+                fp8_quotient_codes<FMT, H, CL>(v, s, 1.0f, d);
+            } else {                          // tiny scale: x * 2^64 and s * 2^64 are exact
+                float sk[H];
 #pragma unroll
-            for (int h = 0; h < H; ++h) sk[h] = s[h] * 0x1p64f;
-            fp8_quotient_codes<FMT, H, CL>(v, sk, 0x1p64f, d);
+                for (int h = 0; h < H; ++h) sk[h] = s[h] * 0x1p64f;
+                fp8_quotient_codes<FMT, H, CL>(v, sk, 0x1p64f, d);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) d[i] &= keep_mask(sc, i / 4);

@@ -213,8 +213,9 @@ __device__ __forceinline__ void accumulate(const LaneBlock<FMT, SC, BL>& b, floa
 }
 
 // Quantize the lane's 32 values (held at 2^-P of their value) into its code
-// words and scale bits (in registers).
-template <int FMT, int SC, int BL, int P = 0>
+// words and scale bits (in registers).  NARROW: the values are widened bf16
+// or fp16 (at most 11 significant bits), which the FP8 encoder exploits.
+template <int FMT, int SC, int BL, int P = 0, bool NARROW = false>
 __device__ __forceinline__ LaneBlock<FMT, SC, BL> encode_lane(const float (&v)[32])
 {
     constexpr int H = Halves<BL>::v;
@@ -232,7 +233,7 @@ __device__ __forceinline__ LaneBlock<FMT, SC, BL> encode_lane(const float (&v)[3
     } else if constexpr (FMT == kInt4) {
         int4_encode<H, P>(v, sc, b.c.d);
     } else if constexpr (FMT == kFp8 || FMT == kBf8) {
-        fp8_encode<FMT, SC, H>(v, sc, b.c.d);
+        fp8_encode<FMT, SC, H, NARROW>(v, sc, b.c.d);
     } else {
         mx_encode<H>(v, sc, b.c.d);
     }
@@ -270,10 +271,10 @@ __device__ __forceinline__ void store_lane_block(const LaneBlock<FMT, SC, BL>& b
     }
 }
 
-template <int FMT, int SC, int BL, int P = 0>
+template <int FMT, int SC, int BL, int P = 0, bool NARROW = false>
 __device__ __forceinline__ void encode_store_buf(const float (&v)[32], Rsrc r, uint32_t lane)
 {
-    store_lane_block<FMT, SC, BL>(encode_lane<FMT, SC, BL, P>(v), r, lane);
+    store_lane_block<FMT, SC, BL>(encode_lane<FMT, SC, BL, P, NARROW>(v), r, lane);
 }
 
 __device__ __forceinline__ void wave_lds_sync()
@@ -374,7 +375,7 @@ __device__ __forceinline__ void quant_tile_chunks(u32x4 (&c)[CPB], uint8_t* lds,
     for (int i = 0; i < CPB; ++i) c[i] = *reinterpret_cast<const u32x4*>(lds + lane * ROW + 16 * i);
     float v[32];
     widen_chunks<DT, CPB>(c, v);
-    encode_store_buf<FMT, SC, BL>(v, span_rsrc(out, tile * TB, TB), lane);
+    encode_store_buf<FMT, SC, BL, 0, DT != kF32>(v, span_rsrc(out, tile * TB, TB), lane);
 }
 
 // Tiles per wave iteration of the quantize kernel with 16-bit input: with
@@ -464,12 +465,12 @@ void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict_
         for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, lane * BB + 16u * i, 0, kNT);
 #endif
         widen_chunks<DT, CPB>(c, v);
-        encode_store_buf<FMT, SC, BL>(v, span_rsrc(out, tile * TB, TB), lane);
+        encode_store_buf<FMT, SC, BL, 0, DT != kF32>(v, span_rsrc(out, tile * TB, TB), lane);
     }
     if (full != tiles && full % tw.stride == tw.first) {     // the partial last tile
         float v[32];
         load_block<DT>(in, full * kTile + (size_t)lane * 32, n, v);
-        encode_store_buf<FMT, SC, BL>(v, span_rsrc(out, full * TB, TB), lane);
+        encode_store_buf<FMT, SC, BL, 0, DT != kF32>(v, span_rsrc(out, full * TB, TB), lane);
     }
 }
 
@@ -805,7 +806,7 @@ void allreduce_kernel(StreamPtrs msgs, int k, size_t n, void* __restrict__ out, 
             float v[32];
             if (!partial) load_lane_row<DT>(msgs.p[j], tile, lane, lds, v);
             else load_block<DT>(msgs.p[j], tile * kTile + (size_t)lane * 32, n, v);
-            const LaneBlock<FMT, SC, BL> b = encode_lane<FMT, SC, BL>(v);
+            const LaneBlock<FMT, SC, BL> b = encode_lane<FMT, SC, BL, 0, DT != kF32>(v);
             if (j == 0) accumulate<FMT, SC, BL, true>(b, acc);
             else accumulate<FMT, SC, BL, false>(b, acc);
         }

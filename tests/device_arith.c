@@ -24,14 +24,27 @@
  *            plus binary32 x within 16 ulp of every half step of every
  *            scale, plus random binary32 x.  For every scale r_lo >= 0, and
  *            y of -0 is -0 (the sign plane keeps the sign of a -0 element).
- *   fp8      the round-to-odd quotient sequence (y0 = |x| rs, y1 = y0 +
- *            fma(-y0, s, |x|) rs, side from fma(-y1, s, |x|), then
- *            round-to-odd, clamp with FP16 scales) followed by the RNE
- *            conversion to E4M3 / E5M2: equal to the RNE code of the exact
- *            quotient, for binary32 x within 16 ulp of every rounding
- *            midpoint (and of the saturation point) of the format, over
- *            random FP32 scales, scales below 2^-64 (x and s times 2^64),
- *            and every fp16 scale, with rs either binary32 neighbour of 1/s.
+ *   fp8narrow  inputs of at most 11 significant bits (bf16, fp16): every
+ *            pair x <= a (a the block maximum), FP32 and FP16 scales, both
+ *            formats, both reciprocal neighbours.  Where the bracket is
+ *            undecided the code follows the block rule (FP32 scale: upper
+ *            code when a - s fmax > 0, lower when < 0, even when 0; FP16
+ *            scale: even) and equals the exact code.
+ *   fp8      two stages.  The bracket: x times the hardware reciprocal
+ *            rounded down and up by 2^-21 (clamped with FP16 scales), both
+ *            products converted; where the codes agree that is the code.
+ *            Else (and for scales below 2^-64) the round-to-odd quotient
+ *            sequence (y1 = fma(|x|, rs, |x| rl) with rl = fma(-s, rs, 1) rs,
+ *            side from the sign bit of fma(-y1, s, |x|), then round-to-odd,
+ *            clamp with FP16 scales) followed by the RNE conversion to E4M3
+ *            / E5M2.  Together equal to the RNE code of the exact quotient,
+ *            for binary32 x within 16 ulp of every rounding midpoint (and of
+ *            the saturation point), random x up to the block maximum and in
+ *            the subnormal range, x far into saturation (FP16 scales), over
+ *            random FP32 scales up to 2^119, scales below 2^-64 (x and s
+ *            times 2^64), and every fp16 scale, with rs either binary32
+ *            neighbour of 1/s.  No product converted by the bracket may lie
+ *            beyond the format's finite range.
  *
  * Usage: device_arith <check> [threads]; prints one line per check and exits
  * 0 when no case differs.
@@ -295,14 +308,18 @@ static void *int_random_worker(void *p)
 
 /* ------------------------------------------------------------------- fp8 */
 
-/* the kernel's round-to-odd quotient of |x| / s (sign dropped: x >= 0) */
+/* the kernel's round-to-odd quotient of |x| / s (sign dropped: x >= 0): the
+ * quotient from the hardware reciprocal rs and its low part rl =
+ * fma(-s, rs, 1) rs, the exact residual's sign bit steps it down one binary32
+ * value, and an inexact result gets its last bit set */
 static float ro_quotient(float ax, float s, float rs, float fmax, int clamp)
 {
-    const float y0 = ax * rs;
-    const float y1 = fmaf(fmaf(-y0, s, ax), rs, y0);
+    const float rl = fmaf(-s, rs, 1.0f) * rs;
+    const float y1 = fmaf(ax, rs, ax * rl);
     const float r = fmaf(-y1, s, ax);
-    uint32_t t = f2u(y1);
-    t = (t - (r < 0.0f ? 1u : 0u)) | (r != 0.0f ? 1u : 0u);
+    const uint32_t rb = f2u(r);
+    uint32_t t = f2u(y1) - (rb >> 31);
+    t |= rb < 1u ? rb : 1u;
     const float yo = u2f(t);
     return clamp ? fminf(yo, fmax) : yo;
 }
@@ -320,13 +337,34 @@ static int fp8_convert(float y, int e5)
     return nearest_tab(tab, cnt, (double)y, 1.0);
 }
 
-/* kernel: x and s below 2^-64 are multiplied by 2^64 first */
+/* how often the bracket gave one code or fell back (per thread, summed at
+ * the end of each worker) */
+static _Thread_local unsigned long long fp8_fast_hits, fp8_fallbacks;
+static _Atomic unsigned long long fp8_fast_total, fp8_fallback_total;
+
+/* kernel: first the bracket, x times the reciprocal rounded down and up by
+ * 2^-21 (clamped to the largest magnitude with FP16 scales); when both
+ * products convert to one code that is the code.  Otherwise, and for scales
+ * below 2^-64, the round-to-odd quotient (x and s below 2^-64 multiplied by
+ * 2^64 first).  A product whose conversion leaves the finite range is a
+ * failure: the kernel must never convert it. */
 static int fp8_device(float x, float s, int which_rcp, int e5, int clamp)
 {
     const float fmax = e5 ? 57344.0f : 448.0f;
+    float c[2];
+    if (s >= 0x1p-64f) {
+        const int nc = rcp_candidates(s, c);
+        const float rs = c[which_rcp < nc ? which_rcp : 0];
+        const float rlo = rs * 0x1.fffffp-1f, rhi = rs * 0x1.000008p0f;
+        float a = x * rlo, b = x * rhi;
+        if (clamp) { a = fminf(a, fmax); b = fminf(b, fmax); }
+        const int ca = fp8_convert(a, e5), cb = fp8_convert(b, e5);
+        if (ca < 0 || cb < 0) return -2;
+        if (ca == cb) { fp8_fast_hits++; return ca; }
+        fp8_fallbacks++;
+    }
     float kx = x, ks = s;
     if (s < 0x1p-64f) { kx = x * 0x1p64f; ks = s * 0x1p64f; }
-    float c[2];
     const int nc = rcp_candidates(ks, c);
     const float rs = c[which_rcp < nc ? which_rcp : 0];
     return fp8_convert(ro_quotient(kx, ks, rs, fmax, clamp), e5);
@@ -361,6 +399,39 @@ static void fp8_one_scale(job *j, float s, int e5, int clamp)
             }
         }
     }
+    /* random magnitudes up to the block maximum (mostly decided by the
+     * bracket), and tiny ones in the format's subnormal range */
+    for (int i = 0; i < 64; ++i) {
+        const uint64_t r = splitmix(&j->seed);
+        const double u = (double)(r >> 11) * 0x1p-53;
+        const double target = (i & 1 ? tab[cnt - 1] * u : tab[3] * u * 4.0) * (double)s;
+        if (target > 3.0e38) continue;
+        const float x = (float)target;
+        const int want = fp8_exact(x, s, e5);
+        for (int w = 0; w < 2; ++w) {
+            j->cases++;
+            if (fp8_device(x, s, w, e5, clamp) != want) j->bad++;
+        }
+    }
+    /* FP16 scales (subnormal, or clamped at 65504) leave quotients far above
+     * the largest magnitude: they saturate, up to the largest binary32 x */
+    if (!clamp) return;
+    for (int k = 1; k < 300; ++k) {
+        const double target = tab[cnt - 1] * (double)s * ldexp(1.0, k);
+        if (target > 3.0e38) break;
+        float x = (float)target;
+        for (int i = 0; i < 4; ++i) x = nextafterf(x, 0.0f);
+        for (int i = 0; i <= 8; ++i, x = nextafterf(x, INFINITY)) {
+            for (int w = 0; w < 2; ++w) {
+                j->cases++;
+                if (fp8_device(x, s, w, e5, clamp) != cnt - 1) j->bad++;
+            }
+        }
+    }
+    for (int w = 0; w < 2; ++w) {
+        j->cases++;
+        if (fp8_device(3.4028234663852886e38f, s, w, e5, clamp) != cnt - 1) j->bad++;
+    }
 }
 
 static void *fp8_worker(void *p)
@@ -374,11 +445,139 @@ static void *fp8_worker(void *p)
         }
         /* random normal FP32 scale (mode 0) or one below 2^-64 (mode 1) */
         const uint64_t r = splitmix(&j->seed);
-        const int ex = mode == 0 ? (int)(r % 200) - 100 : -126 + (int)(r % 62);
+        /* normal scales up to RN32(FLT_MAX / 448) < 2^120 */
+        const int ex = mode == 0 ? (int)(r % 184) - 64 : -126 + (int)(r % 62);
         const float s = ldexpf(1.0f + (float)((r >> 8) & 0x7FFFFF) * 0x1p-23f, ex);
         fp8_one_scale(j, s, e5, 0);
     }
+    fp8_fast_total += fp8_fast_hits;
+    fp8_fallback_total += fp8_fallbacks;
+    fp8_fast_hits = fp8_fallbacks = 0;
     return NULL;
+}
+
+/* ------------------------------------------------------------ fp8narrow */
+
+/* RNE E4M3 / E5M2 code of a binary32 y >= 0 by bit arithmetic (normal
+ * range: carry into the kept mantissa bits, ties to the even one; subnormal
+ * range: y times 2^9 (2^16) rounded to an integer by the 2^23 addition);
+ * -1 at or above the midpoint past the largest magnitude.  Checked against
+ * the table search fp8_convert before use. */
+static int fp8_fast_code(float y, int e5)
+{
+    if (y >= (e5 ? 61440.0f : 464.0f)) return -1;
+    const uint32_t u = f2u(y);
+    if (y >= (e5 ? 0x1p-14f : 0x1p-6f)) {
+        const int sh = e5 ? 21 : 20;
+        const uint32_t t = u + ((1u << (sh - 1)) - 1u) + ((u >> sh) & 1u);
+        return (int)(t >> sh) - (e5 ? 448 : 960);
+    }
+    volatile float k = y * (e5 ? 0x1p16f : 0x1p9f);
+    volatile float r = (k + 0x1p23f) - 0x1p23f;
+    return (int)r;
+}
+
+static float narrow_value(uint16_t b, int fp16)
+{
+    return fp16 ? half_value(b) : u2f((uint32_t)b << 16);
+}
+
+/* RN of a binary32 value in [0, 65504] to fp16, as a binary32 value */
+static float round_to_half(float v)
+{
+    double q = (v >= 0x1p-14f) ? ldexp(1.0, (int)floor(log2((double)v)) - 10) : 0x1p-24;
+    if (v >= 0x1p-14f && ldexp(1.0, (int)floor(log2((double)v))) > v) q *= 0.5;   /* log2 rounding guard */
+    return (float)(nearbyint((double)v / q) * q);
+}
+
+/* Inputs of at most 11 significant bits (bf16, fp16): every (x, block
+ * maximum a) pair, x <= a.  The bracket's undecided pairs must be exact ties
+ * (fmax x = m a with an FP32 scale, x = m s with an FP16 one), resolved per
+ * block: FP32 scale by the sign of a - s fmax (s rounded down: the quotient
+ * lies above the midpoint), FP16 scale to the even code.  Job arg bits:
+ * 0 = fp16 inputs, 1 = E5M2, 2 = FP16 scale. */
+static _Atomic unsigned long long narrow_undecided;
+
+static void *fp8narrow_worker(void *p)
+{
+    job *j = p;
+    const int fp16 = j->arg & 1, e5 = (j->arg >> 1) & 1, s16 = (j->arg >> 2) & 1;
+    const float fmax = e5 ? 57344.0f : 448.0f;
+    unsigned long long und = 0;
+    for (uint64_t ai = j->lo; ai < j->hi; ++ai) {
+        const uint16_t ab = (uint16_t)(ai + 1);
+        const float a = narrow_value(ab, fp16);
+        float sc, dir;
+        if (!s16) {
+            sc = a / fmax;
+            if (!(sc >= 0x1p-64f)) continue;     /* zero block, or the 2^64 path */
+            dir = fmaf(-sc, fmax, a);
+        } else {
+            sc = round_to_half(fminf(a / fmax, 65504.0f));
+            if (sc == 0.0f) continue;
+            dir = 0.0f;
+        }
+        float c[2];
+        const int nc = rcp_candidates(sc, c);
+        for (int w = 0; w < nc; ++w) {
+            const float rlo = c[w] * 0x1.fffffp-1f, rhi = c[w] * 0x1.000008p0f;
+            for (uint32_t xb = 0; xb <= ab; ++xb) {
+                const float x = narrow_value((uint16_t)xb, fp16);
+                float lo = x * rlo, hi = x * rhi;
+                if (s16) { lo = fminf(lo, fmax); hi = fminf(hi, fmax); }
+                const int cl = fp8_fast_code(lo, e5), ch = fp8_fast_code(hi, e5);
+                j->cases++;
+                if (cl < 0 || ch < 0) { j->bad++; continue; }
+                int code = cl;
+                if (cl != ch) {
+                    und++;
+                    if (ch != cl + 1) { j->bad++; continue; }
+                    code = dir > 0.0f ? ch : (dir < 0.0f ? cl : ((cl & 1) ? ch : cl));
+                } else if ((xb & 63u) != 7u) {
+                    continue;                     /* decided: the enclosure check covers it; sample 1/64 */
+                }
+                if (code != fp8_exact(x, sc, e5)) j->bad++;
+            }
+        }
+    }
+    narrow_undecided += und;
+    return NULL;
+}
+
+/* the table search, out of range (-1) from the midpoint past the largest
+ * magnitude on: 464 for E4M3, whose next code point is NaN */
+static int fast_code_want(float y, int e5)
+{
+    return y >= (e5 ? 61440.0f : 464.0f) ? -1 : fp8_convert(y, e5);
+}
+
+/* the bit-arithmetic conversion against the table search */
+static uint64_t check_fast_code(uint64_t *cases)
+{
+    uint64_t bad = 0, seed = 12345;
+    *cases = 0;
+    for (int e5 = 0; e5 < 2; ++e5) {
+        const double *tab = e5 ? e5m2_tab : e4m3_tab;
+        const int cnt = e5 ? 124 : 127;
+        for (int cc = 0; cc < cnt; ++cc) {                 /* around every code and midpoint */
+            const double pts[2] = {tab[cc], cc + 1 < cnt ? 0.5 * (tab[cc] + tab[cc + 1]) : tab[cc] * 1.0625};
+            for (int p = 0; p < 2; ++p) {
+                float y = (float)pts[p];
+                for (int i = 0; i < 8; ++i) y = nextafterf(y, 0.0f);
+                for (int i = 0; i <= 16; ++i, y = nextafterf(y, INFINITY)) {
+                    ++*cases;
+                    if (fp8_fast_code(y, e5) != fast_code_want(y, e5)) ++bad;
+                }
+            }
+        }
+        for (int i = 0; i < 4000000; ++i) {                /* random binary32 below the top */
+            const uint64_t r = splitmix(&seed);
+            const float y = u2f((uint32_t)(r % (f2u(e5 ? 65536.0f : 512.0f))));
+            ++*cases;
+            if (fp8_fast_code(y, e5) != fast_code_want(y, e5)) ++bad;
+        }
+    }
+    return bad;
 }
 
 /* ------------------------------------------------------------------- main */
@@ -391,7 +590,7 @@ static int report(const char *name, uint64_t bad, uint64_t cases)
 
 int main(int argc, char **argv)
 {
-    if (argc < 2) { fprintf(stderr, "usage: %s div|recip|int|fp8 [threads]\n", argv[0]); return 2; }
+    if (argc < 2) { fprintf(stderr, "usage: %s div|recip|int|fp8|fp8narrow [threads]\n", argv[0]); return 2; }
     const int T = argc > 2 ? atoi(argv[2]) : 8;
     init_tables();
     int fail = 0;
@@ -444,6 +643,22 @@ int main(int argc, char **argv)
             bad = run_parallel(fp8_worker, n, T, m, &cases);
             fail |= report(names[m], bad, cases);
         }
+        printf("bracket decided %llu, fell back %llu\n", (unsigned long long)fp8_fast_total,
+               (unsigned long long)fp8_fallback_total);
+    } else if (!strcmp(argv[1], "fp8narrow")) {
+        init_tables();
+        bad = check_fast_code(&cases);
+        fail |= report("fp8 bit-arith conversion", bad, cases);
+        static const char *names[8] = {"bf16 e4m3 fp32 scale", "fp16 e4m3 fp32 scale", "bf16 e5m2 fp32 scale",
+                                       "fp16 e5m2 fp32 scale", "bf16 e4m3 fp16 scale", "fp16 e4m3 fp16 scale",
+                                       "bf16 e5m2 fp16 scale", "fp16 e5m2 fp16 scale"};
+        for (int m = 0; m < 8; ++m) {
+            const uint64_t n = (m & 1) ? 0x7BFF : 0x7F7F;     /* positive finite maxima */
+            bad = run_parallel(fp8narrow_worker, n, T, m, &cases);
+            fail |= report(names[m], bad, cases);
+        }
+        printf("undecided pairs resolved per block %llu\n", (unsigned long long)narrow_undecided);
+        fail |= narrow_undecided == 0;
     } else {
         return 2;
     }

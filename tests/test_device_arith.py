@@ -12,9 +12,21 @@ fmaf and compares it with the exact rule it stands for):
   every bf16 x a block can hold, binary32 x within 16 ulp of every half step
   of every scale, random binary32 x -- while the single product x r differs
   there (control);
-* ``fp8``: the round-to-odd quotient sequence followed by the RNE conversion
-  equals the RNE E4M3 / E5M2 code of the exact quotient next to every
-  rounding midpoint, for FP32 scales (also below 2^-64) and every fp16 scale.
+* ``fp8``: the encoder's two stages together equal the RNE E4M3 / E5M2 code
+  of the exact quotient next to every rounding midpoint, at random
+  magnitudes and far into saturation, for FP32 scales (also below 2^-64) and
+  every fp16 scale.  The first stage converts x times the reciprocal rounded
+  down and up by 2^-21 and keeps the code where both agree; the second, the
+  round-to-odd quotient followed by the RNE conversion, decides the rest.
+  Both stages must be exercised.
+* ``fp8narrow``: for inputs of at most 11 significant bits (every bf16 and
+  every fp16 pair x <= a, a the block maximum; FP32 and FP16 scales; both
+  formats; both reciprocal neighbours) the bracket's undecided elements are
+  exact ties, and the per-block rule gives the code of the exact quotient:
+  the upper code when a - s fmax > 0 (FP32 scale rounded down), the lower
+  when < 0, the even one when the quotient is the midpoint itself.  Every
+  undecided pair is compared with the exact code, and a sample of the
+  decided ones.
 
 The scale rules are those of "QuickReduce INT3 Quantization and Benchmarking
 on MI355" (Method: block FP16 scale) and "RCCLX: Innovating GPU
@@ -43,7 +55,7 @@ def checker(tmp_path_factory):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("check", ["recip", "div", "int", "fp8"])
+@pytest.mark.parametrize("check", ["recip", "div", "int", "fp8", "fp8narrow"])
 def test_device_arithmetic_equals_exact_rule(checker, check):
     threads = str(min(16, os.cpu_count() or 4))
     r = subprocess.run([checker, check, threads], capture_output=True, text=True, timeout=900)
@@ -51,3 +63,9 @@ def test_device_arithmetic_equals_exact_rule(checker, check):
     assert r.returncode == 0, r.stdout + r.stderr
     lines = [ln for ln in r.stdout.splitlines() if "cases" in ln]
     assert lines and all(" differ 0" in ln for ln in lines if "must differ" not in ln)
+    if check == "fp8narrow":
+        res = [ln.split() for ln in r.stdout.splitlines() if ln.startswith("undecided pairs")]
+        assert res and int(res[0][-1]) > 0
+    if check == "fp8":
+        stage = [ln.split() for ln in r.stdout.splitlines() if ln.startswith("bracket decided")]
+        assert stage and int(stage[0][2].rstrip(",")) > 0 and int(stage[0][5]) > 0
