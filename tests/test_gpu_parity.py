@@ -14,6 +14,7 @@ import torch
 import datagen
 import oracle
 import reduction_codec_amd as rca
+from tests import fp8_ties
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -516,6 +517,38 @@ def test_variant_reduce_bit_exact(name, k):
     assert_sums(sums.cpu().numpy(), ref_sum)
 
 
+FP8_SCALED = [n for n in VARIANTS if n.startswith(("e4m3_f", "e5m2_f"))]      # FP32 and FP16 scales
+
+
+def fp8_tie_values(name: str, dt: str, n: int, seed: int) -> np.ndarray:
+    """n values of dt (bf16 bit patterns, float16 or float32) in blocks with
+    planted exact FP8 midpoint ties; fp32 messages hold bf16-valued ties."""
+    elem, scale, b = name.split("_")
+    x, _ = fp8_ties.tie_message(elem, scale, "fp16" if dt == "fp16" else "bf16", int(b[1:]), n, seed)
+    return datagen.narrow(x, dt)
+
+
+@pytest.mark.parametrize("name", FP8_SCALED)
+@pytest.mark.parametrize("dt", DTYPES)
+def test_fp8_exact_midpoint_ties(name, dt):
+    """Blocks whose quotients land exactly on FP8 rounding midpoints, on every
+    side of the scale's rounding: bf16 / fp16 input takes the encoder's
+    per-block tie rule, fp32 input (the same values) its exact fallback; then
+    a 2-stream reduce of the packed stream with itself, whose sums are twice
+    decoded values and so ties again."""
+    n = 3 * 2048 + 320
+    say(f"case fp8 ties {name} dt={dt} n={n}")
+    xs = fp8_tie_values(name, dt, n, seed=len(name) * 101 + DTYPES.index(dt))
+    oc, c = oracle.ALL_CODECS[name], rca.ALL_CODECS[name]
+    ref = oracle.quantize_pack(oc, xs, dtype=ORACLE_DT[dt])
+    assert_same(host_u8(rca.quantize_pack(to_dev(xs, dt), c)), ref, f"{name} codes")
+    want, want_sum = oracle.dequant_reduce_requant(oc, [ref, ref], n, want_sum=True)
+    dref = torch.from_numpy(ref).to(DEV)
+    out, sums = rca.dequant_reduce_requant([dref, dref], c, n, sum_out=True)
+    assert_same(host_u8(out), want, f"{name} reduce of two equal streams")
+    assert_sums(sums.cpu().numpy(), want_sum)
+
+
 @pytest.mark.parametrize("name", [n for n in VARIANTS if n.startswith(("int4_e8m0", "int3_e8m0"))])
 @pytest.mark.parametrize("k", [2, 3, 4])
 def test_int_e8m0_reduce_huge_block_exponents(name, k):
@@ -558,6 +591,28 @@ def test_allreduce_emulate_bit_exact(fmt, dt, two_shot, k):
     g = out.cpu()
     g = g.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else g.numpy()
     assert_same(g, ref, f"allreduce {fmt} {dt}")
+    if two_shot:
+        assert_same(host_u8(packed), ref_packed, "packed sum")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("two_shot", [True, False])
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_allreduce_emulate_fp8_ties(dt, two_shot, k):
+    """The fused kernel's FP8 encodes on messages with planted exact midpoint
+    ties (per-rank encodes of bf16 / fp16 take the per-block tie rule); the
+    second message repeats the first, so the sums hold ties as well."""
+    n = 2 * 2048 + 640
+    say(f"case allreduce fp8 ties dt={dt} two_shot={two_shot} k={k}")
+    msgs = [fp8_tie_values("e4m3_f32_b32", dt, n, seed=900 + j) for j in range(k)]
+    if k >= 2:
+        msgs[1] = msgs[0].copy()
+    ref, ref_packed = oracle.allreduce_emulate(oracle.CODECS["fp8"], msgs, ORACLE_DT[dt], two_shot=two_shot)
+    out, packed = rca.allreduce_emulate([to_dev(m, dt) for m in msgs], rca.FP8, two_shot=two_shot,
+                                        packed_out=two_shot)
+    g = out.cpu()
+    g = g.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else g.numpy()
+    assert_same(g, ref, f"allreduce fp8 ties {dt}")
     if two_shot:
         assert_same(host_u8(packed), ref_packed, "packed sum")
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE = os.path.join(ROOT, "oracle")
 PIN_SUITES = ["tests/test_oracle_formats.py", "tests/test_oracle_quant.py",
               "tests/test_oracle_reduce.py", "tests/test_oracle_variants.py",
-              "tests/test_oracle_fuzz.py"]
+              "tests/test_oracle_fuzz.py", "tests/test_oracle_fp8_ties.py"]
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fno-tree-vectorize",
           "-fPIC", "-shared"]
 
@@ -44,6 +44,10 @@ MUTANTS = {
     "mx_exponent_off_by_one": ("return rco_e8m0_exponent(amax, 2);", "return rco_e8m0_exponent(amax, 1);"),
     "fp8_single_plane_order": ("return e < 16 ? 16 * g + e : 1024 + 16 * g + (e - 16);", "return i;"),
     "int3_pair_order_swapped": ("4 * (p / 2) + 2 * (e % 2);", "4 * (p / 2) + 2 * (1 - e % 2);"),
+    "minifloat_ties_away_from_zero": ("return (c % 2 == 0) ? c : c + 1;", "return c + 1;"),
+    "fp8_quotient_rounded_to_binary32_first": (
+        "(unsigned)mag_of(fabs((double)vb[e]), den));",
+        "(unsigned)mag_of((double)(float)(fabs((double)vb[e]) / den), 1.0));"),
 }
 
 
