@@ -17,8 +17,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE = os.path.join(ROOT, "oracle")
 PIN_SUITES = ["tests/test_oracle_formats.py", "tests/test_oracle_quant.py",
-              "tests/test_oracle_reduce.py", "tests/test_oracle_variants.py",
-              "tests/test_oracle_fuzz.py", "tests/test_oracle_fp8_ties.py"]
+              "tests/test_oracle_fp8_ties.py", "tests/test_oracle_reduce.py",
+              "tests/test_oracle_variants.py", "tests/test_oracle_fuzz.py"]
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fno-tree-vectorize",
           "-fPIC", "-shared"]
 

@@ -103,6 +103,31 @@ def test_int_half_steps_by_construction(qmax):
     assert (oracle.int_mag(np.nextafter(v, np.float32(0)), s, qmax) == qmax).all()
 
 
+@pytest.mark.parametrize("el,qmax", [(oracle.FMT_INT4, 7), (oracle.FMT_INT3, 3)])
+def test_e8m0_int_half_steps_go_to_even(el, qmax):
+    """INT codes with a power-of-two (E8M0) scale S: a block whose maximum is
+    (qmax - 1/2) S has scale S (the maximum lies in [2^k, 2^(k+1)) S with
+    k = floor(log2 qmax)), and its exact half steps (j + 1/2) S decode to the
+    even one of j, j + 1 times S, with the sign kept ("Microscaling Data
+    Formats for Deep Learning", abstract: narrow integer elements under a
+    shared power-of-two scale; ties to even as for every rounding here)."""
+    c = (el, oracle.SCALE_E8M0, 32)
+    blocks = []
+    want = []
+    for e in (-30, -3, 0, 5, 40):
+        S = 2.0 ** e
+        halves = [(j + 0.5) * S for j in range(qmax)]
+        vals = [(qmax - 0.5) * S] + [h * sgn for h in halves for sgn in (1, -1)]
+        vals += [0.0] * (32 - len(vals))
+        blocks.append(vals)
+        want.append([(qmax - 1 if (qmax - 1) % 2 == 0 else qmax) * S] +
+                    [sgn * (j if j % 2 == 0 else j + 1) * S for j in range(qmax) for sgn in (1, -1)] +
+                    [0.0] * (32 - 1 - 2 * qmax))
+    v = np.array(blocks, dtype=np.float32).reshape(-1)
+    d = oracle.unpack_dequant(c, oracle.quantize_pack(c, v), v.size, oracle.DT_FP32)
+    assert np.array_equal(d, np.array(want, dtype=np.float32).reshape(-1))
+
+
 def test_scale_rules_vs_numpy():
     a = np.concatenate([np.abs(RNG.standard_normal(20000)) * 10.0 ** RNG.integers(-12, 7, 20000),
                         [0.0, 1e-45, 3 * 2**-25, 3 * 65504, 7 * 65504, 3e38, 6.1e-5]]).astype(np.float32)
