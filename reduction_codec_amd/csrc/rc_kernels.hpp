@@ -51,9 +51,6 @@
 #ifndef RC_QUANT_F32_WAVES
 #define RC_QUANT_F32_WAVES 4                       // fp32 quantize occupancy target (5, 6: no gain)
 #endif
-#ifndef RC_QUANT_PAIR
-#define RC_QUANT_PAIR 0                            // 16-bit quantize: two tiles per wave iteration, loads first
-#endif
 #ifndef RC_QUANT_LDS
 #define RC_QUANT_LDS 1                             // quantize input regrouped through LDS
 #endif
@@ -356,33 +353,6 @@ template <int FMT, int DT> struct QuantWaves {
 // through buffer stores.  Latency is covered by the other waves of the SIMD
 // (no in-wave prefetch).  The partial last tile, if any, is done after the
 // loop by the wave whose walk would reach it.
-// The tile's 16-byte input chunks (chunk 64 i + lane of the tile in c[i])
-// regrouped through the wave's padded LDS rows so that lane l holds its own
-// block's chunks, widened, encoded and stored (16-bit input).
-template <int FMT, int SC, int BL, int DT, int CPB, int ROW>
-__device__ __forceinline__ void quant_tile_chunks(u32x4 (&c)[CPB], uint8_t* lds, uint32_t lane, uint8_t* __restrict__ out,
-                                                  size_t tile)
-{
-    constexpr int TB = TileGeom<FMT, SC, BL>::bytes;
-    wave_lds_sync();                           // the previous tile's rows are fully read
-#pragma unroll
-    for (int i = 0; i < CPB; ++i) {
-        const uint32_t ch = 64u * i + lane;
-        *reinterpret_cast<u32x4*>(lds + (ch / CPB) * ROW + (ch % CPB) * 16) = c[i];
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int i = 0; i < CPB; ++i) c[i] = *reinterpret_cast<const u32x4*>(lds + lane * ROW + 16 * i);
-    float v[32];
-    widen_chunks<DT, CPB>(c, v);
-    encode_store_buf<FMT, SC, BL, 0, DT != kF32>(v, span_rsrc(out, tile * TB, TB), lane);
-}
-
-// Tiles per wave iteration of the quantize kernel with 16-bit input: with
-// two, a wave issues the loads of both its tiles before it encodes either,
-// so the second tile's data is in flight while the first is encoded.
-template <int DT> struct QuantPair { static constexpr int v = (DT != kF32 && RC_QUANT_PAIR) ? 2 : 1; };
-
 template <int FMT, int SC, int BL, int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QuantWaves<FMT, DT>::v)))
 void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict__ out, size_t tiles)
@@ -403,25 +373,6 @@ void quantize_kernel(const void* __restrict__ in, size_t n, uint8_t* __restrict_
     constexpr int ROWS = HALVES ? 32 : 64;
     __shared__ __attribute__((aligned(16))) uint8_t sm[kWavesPerGroup][ROWS * ROW];
     uint8_t* lds = sm[tw.w];
-#endif
-#if RC_QUANT_LDS
-    if constexpr (QuantPair<DT>::v == 2) {
-        for (size_t tile = tw.first; tile < full; tile += 2 * tw.stride) {
-            const size_t t2 = tile + tw.stride;
-            const bool two = t2 < full;                              // wave-uniform
-            u32x4 c[CPB], c2[CPB];
-            const Rsrc src = span_rsrc(in, tile * TIB, TIB);
-#pragma unroll
-            for (int i = 0; i < CPB; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (64u * i + lane) * 16u, 0, kNT);
-            if (two) {
-                const Rsrc src2 = span_rsrc(in, t2 * TIB, TIB);
-#pragma unroll
-                for (int i = 0; i < CPB; ++i) c2[i] = __builtin_amdgcn_raw_buffer_load_b128(src2, (64u * i + lane) * 16u, 0, kNT);
-            }
-            quant_tile_chunks<FMT, SC, BL, DT, CPB, ROW>(c, lds, lane, out, tile);
-            if (two) quant_tile_chunks<FMT, SC, BL, DT, CPB, ROW>(c2, lds, lane, out, t2);
-        }
-    } else
 #endif
     for (size_t tile = tw.first; tile < full; tile += tw.stride) {
         const Rsrc src = span_rsrc(in, tile * TIB, TIB);
@@ -1056,9 +1007,9 @@ hipError_t launch_quantize_t(int dt, const void* in, size_t n, void* out, hipStr
     const size_t tiles = (n + kTile - 1) / kTile;
     uint8_t* o = static_cast<uint8_t*>(out);
     switch (dt) {
-    case kF32: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF32>), tile_grid((tiles + QuantPair<kF32>::v - 1) / QuantPair<kF32>::v, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
-    case kF16: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF16>), tile_grid((tiles + QuantPair<kF16>::v - 1) / QuantPair<kF16>::v, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
-    default:   hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kBF16>), tile_grid((tiles + QuantPair<kBF16>::v - 1) / QuantPair<kBF16>::v, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
+    case kF32: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF32>), tile_grid(tiles, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
+    case kF16: hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kF16>), tile_grid(tiles, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
+    default:   hipLaunchKernelGGL((quantize_kernel<FMT, SC, BL, kBF16>), tile_grid(tiles, kWavesPerGroup, RC_QUANT_GROUPS_PER_CU), dim3(256), 0, st, in, n, o, tiles); break;
     }
     return hipGetLastError();
 }
