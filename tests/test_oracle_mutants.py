@@ -7,6 +7,7 @@ the oracle package at the broken build).  The suites must fail: a mistake they
 let through would mean the oracle is pinned only to itself in that place.  The
 mistakes are on the CPU only; nothing here touches the GPU or the HIP library.
 """
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -68,16 +69,30 @@ def _build(tmp_path, name):
     return lib
 
 
-@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_reject_mutant(tmp_path, name):
-    lib = _build(tmp_path, name)
+def _run_pins(lib):
     env = dict(os.environ, RC_ORACLE_LIB=str(lib), RC_FUZZ_EXAMPLES="40")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu",
                         "-p", "no:cacheprovider", *PIN_SUITES],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    tail = (r.stdout + r.stderr)[-1500:]
-    assert r.returncode == 1 and " failed" in r.stdout, f"mutant {name} survived the pins:\n{tail}"
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+    return r.returncode, r.stdout, (r.stdout + r.stderr)[-1500:]
+
+
+@pytest.fixture(scope="module")
+def mutant_runs(tmp_path_factory):
+    """Every mutant built, and the pin suites run against each, several at a
+    time (each run is its own process)."""
+    tmp = tmp_path_factory.mktemp("mutants")
+    libs = {name: _build(tmp, name) for name in sorted(MUTANTS)}
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 2)) as ex:
+        futs = {name: ex.submit(_run_pins, lib) for name, lib in libs.items()}
+        return {name: f.result() for name, f in futs.items()}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(mutant_runs, name):
+    rc, out, tail = mutant_runs[name]
+    assert rc == 1 and " failed" in out, f"mutant {name} survived the pins:\n{tail}"
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
