@@ -520,12 +520,13 @@ def test_variant_reduce_bit_exact(name, k):
 FP8_SCALED = [n for n in VARIANTS if n.startswith(("e4m3_f", "e5m2_f"))]      # FP32 and FP16 scales
 
 
-def fp8_tie_values(name: str, dt: str, n: int, seed: int) -> np.ndarray:
+def fp8_tie_values(name: str, dt: str, n: int, seed: int, shift: int = 0) -> np.ndarray:
     """n values of dt (bf16 bit patterns, float16 or float32) in blocks with
-    planted exact FP8 midpoint ties; fp32 messages hold bf16-valued ties."""
+    planted exact FP8 midpoint ties; fp32 messages hold bf16-valued ties.
+    shift scales them by 2^shift (exact for bf16 and fp32 at -80)."""
     elem, scale, b = name.split("_")
     x, _ = fp8_ties.tie_message(elem, scale, "fp16" if dt == "fp16" else "bf16", int(b[1:]), n, seed)
-    return datagen.narrow(x, dt)
+    return datagen.narrow(np.ldexp(x, shift).astype(np.float32), dt)
 
 
 @pytest.mark.parametrize("name", FP8_SCALED)
@@ -539,6 +540,25 @@ def test_fp8_exact_midpoint_ties(name, dt):
     n = 3 * 2048 + 320
     say(f"case fp8 ties {name} dt={dt} n={n}")
     xs = fp8_tie_values(name, dt, n, seed=len(name) * 101 + DTYPES.index(dt))
+    oc, c = oracle.ALL_CODECS[name], rca.ALL_CODECS[name]
+    ref = oracle.quantize_pack(oc, xs, dtype=ORACLE_DT[dt])
+    assert_same(host_u8(rca.quantize_pack(to_dev(xs, dt), c)), ref, f"{name} codes")
+    want, want_sum = oracle.dequant_reduce_requant(oc, [ref, ref], n, want_sum=True)
+    dref = torch.from_numpy(ref).to(DEV)
+    out, sums = rca.dequant_reduce_requant([dref, dref], c, n, sum_out=True)
+    assert_same(host_u8(out), want, f"{name} reduce of two equal streams")
+    assert_sums(sums.cpu().numpy(), want_sum)
+
+
+@pytest.mark.parametrize("name", [n for n in FP8_SCALED if "_f32_" in n])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_fp8_ties_with_scales_below_2_pow_64(name, dt):
+    """The tie messages times 2^-80: block scales from about 2^-108 up, many
+    below 2^-64, where a wave holding such a lane encodes every code with the
+    exact round-to-odd sequence (x and s times 2^64 in those lanes)."""
+    n = 2 * 2048 + 320
+    say(f"case fp8 ties tiny scales {name} dt={dt}")
+    xs = fp8_tie_values(name, dt, n, seed=len(name) * 7 + 5, shift=-80)
     oc, c = oracle.ALL_CODECS[name], rca.ALL_CODECS[name]
     ref = oracle.quantize_pack(oc, xs, dtype=ORACLE_DT[dt])
     assert_same(host_u8(rca.quantize_pack(to_dev(xs, dt), c)), ref, f"{name} codes")

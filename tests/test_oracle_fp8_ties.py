@@ -20,15 +20,23 @@ from tests.fp8_ties import expected_code_index, magnitudes, scale_of, tie_messag
 DT = {"bf16": oracle.DT_BF16, "fp16": oracle.DT_FP16}
 
 
-@pytest.mark.parametrize("elem", ["e4m3", "e5m2"])
-@pytest.mark.parametrize("scale", ["f32", "f16"])
-@pytest.mark.parametrize("dt", ["bf16", "fp16"])
-@pytest.mark.parametrize("block", [16, 32, 64])
-def test_oracle_codes_at_exact_fp8_ties(elem, scale, dt, block):
+CASES = [(e, sc, dt, b, 0) for e in ("e4m3", "e5m2") for sc in ("f32", "f16") for dt in ("bf16", "fp16")
+         for b in (16, 32, 64)]
+# bf16 blocks 2^-80 smaller (exact; every tie and its side is kept): FP32
+# scales down to about 2^-108, many below 2^-64
+CASES += [(e, "f32", "bf16", b, -80) for e in ("e4m3", "e5m2") for b in (16, 32, 64)]
+
+
+@pytest.mark.parametrize("elem,scale,dt,block,shift", CASES)
+def test_oracle_codes_at_exact_fp8_ties(elem, scale, dt, block, shift):
     n = 2048 + 320
     x, info = tie_message(elem, scale, dt, block, n, seed=hash((elem, scale, dt, block)) % 2**32)
+    exact = np.ldexp(x.astype(np.float64), shift)
+    xn = datagen.narrow(exact.astype(np.float32), dt)
+    x = oracle.widen_to_f32(xn, DT[dt])
+    kept = x.astype(np.float64) == exact          # shifted below the normal range: rounded, no tie
     c = oracle.ALL_CODECS[f"{elem}_{scale}_b{block}"]
-    packed = oracle.quantize_pack(c, datagen.narrow(x, dt), dtype=DT[dt])
+    packed = oracle.quantize_pack(c, xn, dtype=DT[dt])
     dec = oracle.unpack_dequant(c, packed, n, oracle.DT_FP32)
     vals = magnitudes(elem)
     ties, sides = 0, set()
@@ -38,9 +46,10 @@ def test_oracle_codes_at_exact_fp8_ties(elem, scale, dt, block):
         if blk.size == 0:
             continue
         a = float(np.abs(blk).max())
+        assert kept[base:base + blk.size][np.abs(blk) == a].all()
         s = scale_of(a, elem, scale)
         for j, (lo, hi) in tie_at.items():
-            if base + j >= n:
+            if base + j >= n or not kept[base + j]:
                 continue
             want = float(np.float32(vals[expected_code_index(lo, hi, side)] * s))
             got = float(dec[base + j])
