@@ -87,3 +87,35 @@ def test_fuzz_quantize_reduce_unpack(name, dt, n, k, seed, kinds):
     ref_y = oracle.unpack_dequant(c_or, ref_out, n, oracle.DT_FP32)
     y = rca.unpack_dequant(out, c, n, torch.float32).cpu().numpy()
     assert ((y.view(np.uint32) == ref_y.view(np.uint32)) | (np.isnan(y) & np.isnan(ref_y))).all(), "unpack"
+
+
+FUSED = ["int4", "int3", "fp8", "mxfp4"]
+
+
+@settings(max_examples=max(1, EXAMPLES // 2), deadline=None, derandomize=EXAMPLES == 120, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(fmt=st.sampled_from(FUSED), dt=st.sampled_from(sorted(DTYPES)),
+       n=st.integers(min_value=1, max_value=3 * 2048 + 200), k=st.integers(min_value=1, max_value=6),
+       two_shot=st.booleans(), seed=st.integers(min_value=0, max_value=2**31 - 1),
+       kinds=st.lists(st.integers(min_value=0, max_value=9), min_size=1, max_size=9))
+def test_fuzz_allreduce_emulate(fmt, dt, n, k, two_shot, seed, kinds):
+    """The one-kernel all-reduce emulation against the oracle's composition
+    (quantize every message, reduce, then unpack the requantized sum or round
+    the FP32 sums to the message dtype), on the same value mixes."""
+    print(f"case fuzz allreduce {fmt} dt={dt} n={n} k={k} two_shot={two_shot} seed={seed} kinds={kinds}",
+          flush=True)
+    rng = np.random.default_rng(seed)
+    xs = [make_values(rng, n, kinds[j % len(kinds):] + kinds[:j % len(kinds)], k, dt) for j in range(k)]
+    ref, ref_packed = oracle.allreduce_emulate(oracle.CODECS[fmt], xs, DTYPES[dt][1], two_shot=two_shot)
+    out, packed = rca.allreduce_emulate([to_dev(x, dt) for x in xs], rca.CODECS[fmt], two_shot=two_shot,
+                                        packed_out=two_shot)
+    g = out.cpu()
+    g = g.numpy() if dt == "fp32" else g.view(torch.int16).numpy().view(np.uint16)
+    r = np.asarray(ref)
+    r = r if dt == "fp32" else r.view(np.uint16)
+    if dt == "fp32":
+        assert ((g.view(np.uint32) == r.view(np.uint32)) | (np.isnan(g) & np.isnan(r))).all(), "output"
+    else:
+        assert np.array_equal(g, r), "output"
+    if two_shot:
+        assert np.array_equal(packed.cpu().numpy(), ref_packed), "packed sum"
