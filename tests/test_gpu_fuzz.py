@@ -119,3 +119,36 @@ def test_fuzz_allreduce_emulate(fmt, dt, n, k, two_shot, seed, kinds):
         assert np.array_equal(g, r), "output"
     if two_shot:
         assert np.array_equal(packed.cpu().numpy(), ref_packed), "packed sum"
+
+
+@settings(max_examples=max(1, EXAMPLES // 3), deadline=None, derandomize=EXAMPLES == 120, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(rows=st.integers(min_value=1, max_value=40), t=st.integers(min_value=1, max_value=5),
+       xt=st.sampled_from(sorted(DTYPES)), yt=st.sampled_from(sorted(DTYPES)),
+       seed=st.integers(min_value=0, max_value=2**31 - 1),
+       wspread=st.integers(min_value=0, max_value=30), xspread=st.integers(min_value=0, max_value=30))
+def test_fuzz_mxfp4_gemv(rows, t, xt, yt, seed, wspread, xspread):
+    """y = W x from MXFP4-packed rows against the exact dot product of the
+    decoded weights and x: |y - W x| <= (38 + T) 2^-24 sum |W_ij x_j| (plus
+    a tiny absolute term), T = cols / 2048, for fp32 y; a bf16 / fp16 y must
+    be that fp32 y rounded to nearest even.  Weights and x span 2^wspread and
+    2^xspread in magnitude."""
+    cols = 2048 * t
+    print(f"case fuzz gemv rows={rows} cols={cols} x={xt} y={yt} seed={seed} w2^{wspread} x2^{xspread}",
+          flush=True)
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(rows * cols) * np.exp2(rng.uniform(-wspread, 0, rows * cols))).astype(np.float32)
+    x = (rng.standard_normal(cols) * np.exp2(rng.uniform(-xspread, 0, cols))).astype(np.float32)
+    xn = datagen.narrow(x, xt)
+    packed = oracle.quantize_pack(oracle.MXFP4, w, dtype=oracle.DT_FP32)
+    exact, mag = oracle.mxfp4_gemv(packed, rows, cols, xn, x_dtype=DTYPES[xt][1])
+    pd, xd = torch.from_numpy(packed).to(DEV), to_dev(xn, xt)
+    y32 = rca.mxfp4_gemv(pd, rows, cols, xd, out_dtype=torch.float32).cpu().numpy()
+    tol = (38 + t) * 2.0 ** -24 * mag + 64 * 2.0 ** -149
+    err = np.abs(y32.astype(np.float64) - exact)
+    assert (err <= tol).all(), float(np.max(err / np.maximum(tol, 1e-300)))
+    if yt != "fp32":
+        y = rca.mxfp4_gemv(pd, rows, cols, xd, out_dtype=DTYPES[yt][0]).cpu().view(torch.int16).numpy().view(np.uint16)
+        with np.errstate(over="ignore"):
+            want = oracle.f32_to_bf16_bits(y32) if yt == "bf16" else oracle.f32_to_f16_bits(y32)
+        assert np.array_equal(y, want), f"{yt} y = RN(fp32 y)"
