@@ -69,3 +69,15 @@ def test_device_arithmetic_equals_exact_rule(checker, check):
     if check == "fp8":
         stage = [ln.split() for ln in r.stdout.splitlines() if ln.startswith("bracket decided")]
         assert stage and int(stage[0][2].rstrip(",")) > 0 and int(stage[0][5]) > 0
+
+
+def test_kernel_uses_the_proved_fp8_constants():
+    """The FP8 encoder in the kernel sources uses the factors and the scale
+    threshold that the fp8 / fp8narrow checks above prove: the reciprocal
+    rounded down and up by 2^-21 (0x1.fffffp-1, 0x1.000008p0) and the exact
+    sequence for scales below 2^-64, in the same binary32 spelling."""
+    dev = open(os.path.join(HERE, "..", "reduction_codec_amd", "csrc", "rc_device.hpp")).read()
+    proof = open(os.path.join(HERE, "device_arith.c")).read()
+    for lit in ("0x1.fffffp-1f", "0x1.000008p0f", "0x1p-64f", "0x1p64f"):
+        assert lit in dev, f"{lit} not in the kernel"
+        assert lit in proof, f"{lit} not in the proof"
