@@ -1,4 +1,4 @@
-"""Exhaustive GPU check of the FP8 encoder on narrow inputs.
+"""Exhaustive GPU check of the exact-quotient encoders on narrow inputs.
 
 For every positive finite bf16 (or fp16) value a, blocks of 32 elements hold
 a followed by every bf16 (fp16) value x in [0, a] (negated at odd positions),
@@ -6,10 +6,13 @@ a followed by every bf16 (fp16) value x in [0, a] (negated at odd positions),
 allows.  The GPU's E4M3 / E5M2 codes with FP32 and FP16 block scales must
 equal the oracle's byte for byte -- the exact-quotient rounding of "FP8
 Formats for Deep Learning" (abstract) under the block scales of "RCCLX:
-Innovating GPU communications on AMD platforms" (Low-Precision Collectives).
-The bf16 pairs also run as fp32 input, which takes the encoder's exact
-fallback wherever a quotient sits on a rounding midpoint.  This checks on the
-hardware what tests/device_arith.c checks by emulation.
+Innovating GPU communications on AMD platforms" (Low-Precision Collectives)
+-- and so must the INT3 / INT4 codes with FP16 block scales (round half to
+even of the exact quotient, "QuickReduce INT3 Quantization and Benchmarking
+on MI355", Method).  The bf16 pairs also run as fp32 input, which takes the
+FP8 encoder's exact fallback wherever a quotient sits on a rounding
+midpoint.  This checks on the hardware what tests/device_arith.c checks by
+emulation.
 """
 import os
 
@@ -24,7 +27,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 TOP = {"bf16": 0x7F7F, "fp16": 0x7BFF}           # largest finite positive bit pattern
 CHUNK_BLOCKS = 1 << 20                             # 32 Mi elements per launch
-# every block maximum (all 12 cases: about 35 s on an MI355X machine);
+# every block maximum (all 18 cases: about 50 s on an MI355X machine);
 # RC_FP8_PAIR_STEP=17 takes every 17th, with every x below it, for a quick run
 A_STEP = int(os.environ.get("RC_FP8_PAIR_STEP", "1"))
 
@@ -50,14 +53,13 @@ def pair_blocks(dt: str):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("elem", ["e4m3", "e5m2"])
-@pytest.mark.parametrize("scale", ["f32", "f16"])
+@pytest.mark.parametrize("name", ["e4m3_f32_b32", "e4m3_f16_b32", "e5m2_f32_b32", "e5m2_f16_b32",
+                                  "int3_f16_b32", "int4_f16_b32"])
 @pytest.mark.parametrize("src,dt", [("bf16", "bf16"), ("fp16", "fp16"), ("bf16", "fp32")])
-def test_fp8_every_narrow_pair(elem, scale, src, dt):
-    name = f"{elem}_{scale}_b32"
+def test_every_narrow_pair(name, src, dt):
     c, oc = rca.ALL_CODECS[name], oracle.ALL_CODECS[name]
     for i, bits in enumerate(pair_blocks(src)):
-        print(f"case fp8 every pair {name} {src} values as {dt}, chunk {i} ({bits.size} elements)", flush=True)
+        print(f"case every pair {name} {src} values as {dt}, chunk {i} ({bits.size} elements)", flush=True)
         if dt == "fp32":
             host = oracle.widen_to_f32(bits, oracle.DT_BF16)
             odt = oracle.DT_FP32
