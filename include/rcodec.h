@@ -53,6 +53,14 @@
  *     saturating at the format's largest magnitude) of v * 2^-e; signs kept.
  *   Reduce: acc = d_0; acc = fp32(acc + d_k) for k = 1..K-1 in stream order;
  *     the sums are requantized with the same codec.
+ *   Decode of any bytes: every bit pattern of codes and scales decodes to
+ *     fp32(code * scale) (NaN and infinite FP8 codes, negative, subnormal and
+ *     non-finite FP16/FP32 scales included), so the decoded values and the
+ *     FP32 sums of arbitrary packed data are defined.  With E8M0 scales the
+ *     product is rounded, so scale bytes the encoder never writes (2^120 and
+ *     up for E4M3, 2^113 for E5M2, 2^126 for INT4 and E2M1, 2^127 for INT3)
+ *     give +-inf where it overflows, and 0xFF gives NaN.  The requantized
+ *     codes of non-finite sums are unspecified.
  *
  * Conventions shared by every entry point:
  *   - Pointers named in/out/ins[k]/sum_out are device pointers (HIP global

@@ -460,7 +460,10 @@ __device__ __forceinline__ Int3Words int3_encode(const float (&v)[32], const Enc
 // times dm = 2S (exact products, one rounding per add); with sums held at
 // half their value, dm = S.  The first term is an fma with a -0 addend,
 // which is the product itself, signed zeros included.
-template <bool FIRST, int H>
+// ROUNDED (E8M0 exponents whose products can exceed binary32): the nibbles
+// decode as q (conversion scale 2), dm = 2^e, and each product is rounded
+// before it is added.
+template <bool FIRST, int H, bool ROUNDED = false>
 __device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32_t h, const float (&dm)[H],
                                                 float (&acc)[32])
 {
@@ -470,8 +473,12 @@ __device__ __forceinline__ void int3_accumulate(uint32_t w0, uint32_t w1, uint32
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float m = dm[H == 2 ? b / 2 : 0];
-            const f2 c = fp4_dec(Ng, 1.0f, b);
-            if (FIRST) {
+            const f2 c = fp4_dec(Ng, ROUNDED ? 2.0f : 1.0f, b);
+            if constexpr (ROUNDED) {
+                const float vx = __fmul_rn(c.x, m), vy = __fmul_rn(c.y, m);
+                acc[8 * b + g] = FIRST ? vx : __fadd_rn(acc[8 * b + g], vx);
+                acc[8 * b + 4 + g] = FIRST ? vy : __fadd_rn(acc[8 * b + 4 + g], vy);
+            } else if (FIRST) {
                 acc[8 * b + g] = __builtin_fmaf(c.x, m, -0.0f);
                 acc[8 * b + 4 + g] = __builtin_fmaf(c.y, m, -0.0f);
             }
@@ -540,7 +547,7 @@ __device__ __forceinline__ void int4_encode(const float (&v)[32], const EncScale
 // acc[e] (+)= q_e * S: the nibbles rebuilt as E4M3 subnormal bytes, decoded
 // times the power-of-two part of `cs` (1 for an FP16 scale, giving q 2^-9,
 // with dm = 512 s; 512 for E8M0, giving q, with dm = 2^e).
-template <bool FIRST, int H>
+template <bool FIRST, int H, bool ROUNDED = false>
 __device__ __forceinline__ void int4_accumulate(const uint32_t (&D)[4], float cs, const float (&dm)[H],
                                                 float (&acc)[32])
 {
@@ -560,8 +567,14 @@ __device__ __forceinline__ void int4_accumulate(const uint32_t (&D)[4], float cs
         const float c[8] = {e01.x, o01.x, e01.y, o01.y, e23.x, o23.x, e23.y, o23.y};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (FIRST) acc[8 * d + j] = __builtin_fmaf(c[j], m, -0.0f);   // the product, signed zeros kept
-            else acc[8 * d + j] = __builtin_fmaf(c[j], m, acc[8 * d + j]);
+            if constexpr (ROUNDED) {
+                const float v = __fmul_rn(c[j], m);
+                acc[8 * d + j] = FIRST ? v : __fadd_rn(acc[8 * d + j], v);
+            } else if (FIRST) {
+                acc[8 * d + j] = __builtin_fmaf(c[j], m, -0.0f);   // the product, signed zeros kept
+            } else {
+                acc[8 * d + j] = __builtin_fmaf(c[j], m, acc[8 * d + j]);
+            }
         }
     }
 }
@@ -753,8 +766,10 @@ __device__ __forceinline__ void fp8_encode(const float (&v)[32], const EncScale 
 }
 
 // acc[e] (+)= code_e * S.  FP32 scale: RN32(code * s) then RN32(acc + d);
-// FP16 and E8M0 scales: code * S is exact, so one fma is the same.
-template <int FMT, int SC, bool FIRST, int H>
+// FP16 and E8M0 scales: code * S is exact, so one fma is the same -- unless
+// it exceeds binary32 (E8M0 exponents the encoder never writes): ROUNDED
+// then rounds each product as with FP32 scales.
+template <int FMT, int SC, bool FIRST, int H, bool ROUNDED = false>
 __device__ __forceinline__ void fp8_accumulate(const uint32_t (&D)[8], const float (&dm)[H], float (&acc)[32])
 {
 #pragma unroll
@@ -764,7 +779,7 @@ __device__ __forceinline__ void fp8_accumulate(const uint32_t (&D)[8], const flo
         const float c[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if constexpr (SC == kS32) {
+            if constexpr (SC == kS32 || ROUNDED) {
                 const float dv = __fmul_rn(c[j], m);                 // RN32(code * s)
                 if (FIRST) acc[4 * d + j] = dv;
                 else acc[4 * d + j] = __fadd_rn(acc[4 * d + j], dv);  // RN32(acc + d)
@@ -792,7 +807,7 @@ __device__ __forceinline__ void mx_encode(const float (&v)[32], const EncScale (
     }
 }
 
-template <bool FIRST, int H>
+template <bool FIRST, int H, bool ROUNDED = false>
 __device__ __forceinline__ void mx_accumulate(const uint32_t (&D)[4], const float (&dm)[H], float (&acc)[32])
 {
 #pragma unroll
@@ -802,6 +817,10 @@ __device__ __forceinline__ void mx_accumulate(const uint32_t (&D)[4], const floa
         for (int b = 0; b < 4; ++b) {
             const f2 c = fp4_dec(D[d], 1.0f, b);            // code value, exact
             if (FIRST) { acc[8 * d + 2 * b] = c.x * p; acc[8 * d + 2 * b + 1] = c.y * p; }
+            else if constexpr (ROUNDED) {                    // the product may exceed binary32
+                acc[8 * d + 2 * b] = __fadd_rn(acc[8 * d + 2 * b], __fmul_rn(c.x, p));
+                acc[8 * d + 2 * b + 1] = __fadd_rn(acc[8 * d + 2 * b + 1], __fmul_rn(c.y, p));
+            }
             else {                                            // c * 2^e is exact: one rounding
                 acc[8 * d + 2 * b] = __builtin_fmaf(c.x, p, acc[8 * d + 2 * b]);
                 acc[8 * d + 2 * b + 1] = __builtin_fmaf(c.y, p, acc[8 * d + 2 * b + 1]);

@@ -188,11 +188,29 @@ template <int FMT, int SC> struct SumScale {
     static constexpr int v = SC == kS16 ? (FMT == kInt3 ? 1 : (FMT == kInt4 ? 9 : 0)) : 0;
 };
 
-// acc (+)= decoded values of the lane's 32 elements (times 2^-P).
-template <int FMT, int SC, int BL, bool FIRST, int P = 0>
+// acc (+)= decoded values of the lane's 32 elements (times 2^-P).  ROUNDED,
+// the default with E8M0 scales: every product is rounded before it is added
+// (one multiply and one add instead of an fma), and INT3 codes decode as q
+// with multiplier 2^e.  The same result as the fma while code * 2^e is a
+// binary32 number, and still the definition where it is not: E8M0 bytes from
+// 2^120 (E4M3), 2^113 (E5M2), 2^126 (INT4, E2M1) or 2^127 (INT3, whose
+// usual multiplier 2^(e + 1) would itself be infinite) on.  The encoder never
+// writes those, but any packed bytes can hold them; the fused kernel, which
+// decodes only its own codes, keeps the fma.
+template <int FMT, int SC, int BL, bool FIRST, int P = 0, bool ROUNDED = (SC == kSE8)>
 __device__ __forceinline__ void accumulate(const LaneBlock<FMT, SC, BL>& b, float (&acc)[32])
 {
     constexpr int H = Halves<BL>::v;
+    if constexpr (SC == kSE8 && ROUNDED) {
+        float dm[H];
+#pragma unroll
+        for (int h = 0; h < H; ++h) dm[h] = e8m0_mult<0>(b.sbits[h]);       // 2^e
+        if constexpr (FMT == kInt3) int3_accumulate<FIRST, H, true>(b.c.w0, b.c.w1, b.c.h, dm, acc);
+        else if constexpr (FMT == kInt4) int4_accumulate<FIRST, H, true>(b.c.d, 512.0f, dm, acc);
+        else if constexpr (FMT == kFp8 || FMT == kBf8) fp8_accumulate<FMT, SC, FIRST, H, true>(b.c.d, dm, acc);
+        else mx_accumulate<FIRST, H, true>(b.c.d, dm, acc);
+        return;
+    }
     float dm[H];
 #pragma unroll
     for (int h = 0; h < H; ++h) dm[h] = dec_mult<FMT, SC, P>(b.sbits[h]);
@@ -758,14 +776,14 @@ void allreduce_kernel(StreamPtrs msgs, int k, size_t n, void* __restrict__ out, 
             if (!partial) load_lane_row<DT>(msgs.p[j], tile, lane, lds, v);
             else load_block<DT>(msgs.p[j], tile * kTile + (size_t)lane * 32, n, v);
             const LaneBlock<FMT, SC, BL> b = encode_lane<FMT, SC, BL, 0, DT != kF32>(v);
-            if (j == 0) accumulate<FMT, SC, BL, true>(b, acc);
-            else accumulate<FMT, SC, BL, false>(b, acc);
+            if (j == 0) accumulate<FMT, SC, BL, true, 0, false>(b, acc);
+            else accumulate<FMT, SC, BL, false, 0, false>(b, acc);
         }
         float d[32];
         if constexpr (TWO_SHOT) {
             const LaneBlock<FMT, SC, BL> r = encode_lane<FMT, SC, BL>(acc);
             if (packed_out) store_lane_block<FMT, SC, BL>(r, span_rsrc(packed_out, tile * TB, TB), lane);
-            accumulate<FMT, SC, BL, true>(r, d);
+            accumulate<FMT, SC, BL, true, 0, false>(r, d);
         } else {
 #pragma unroll
             for (int e = 0; e < 32; ++e) d[e] = acc[e];

@@ -517,6 +517,41 @@ def test_variant_reduce_bit_exact(name, k):
     assert_sums(sums.cpu().numpy(), ref_sum)
 
 
+def same_values(got: np.ndarray, ref: np.ndarray, what: str):
+    """Equal as values: bit for bit, except that any NaN matches any NaN."""
+    g, r = np.asarray(got, dtype=np.float32), np.asarray(ref, dtype=np.float32)
+    ok = (g.view(np.uint32) == r.view(np.uint32)) | (np.isnan(g) & np.isnan(r))
+    if not ok.all():
+        bad = np.nonzero(~ok)[0]
+        raise AssertionError(f"{what}: {bad.size} differ; first (index, got, ref): "
+                             f"{[(int(i), float(g[i]), float(r[i])) for i in bad[:6]]}")
+
+
+@pytest.mark.parametrize("name", VARIANTS)
+def test_decode_of_arbitrary_bytes(name):
+    """Decoding is defined for every bit pattern of codes and scales (NaN,
+    infinite, negative and subnormal scales, FP8 NaN / infinity codes, the
+    E8M0 NaN byte): packed streams of random bytes unpack to fp32, bf16 and
+    fp16, and two of them reduce to the FP32 sums, as the oracle decodes them
+    (a NaN matching any NaN).  The requantized codes of non-finite sums are
+    unspecified and not compared."""
+    n = 16 * 2048 + 100
+    say(f"case decode of arbitrary bytes {name}")
+    oc, c = oracle.ALL_CODECS[name], rca.ALL_CODECS[name]
+    rng = np.random.default_rng(len(name) * 131)
+    streams = [rng.integers(0, 256, oracle.packed_bytes(oc, n), dtype=np.uint8) for _ in range(2)]
+    d0 = torch.from_numpy(streams[0]).to(DEV)
+    same_values(rca.unpack_dequant(d0, c, n, torch.float32).cpu().numpy(),
+                oracle.unpack_dequant(oc, streams[0], n, oracle.DT_FP32), f"{name} -> fp32")
+    for odt, tdt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        g = rca.unpack_dequant(d0, c, n, tdt).cpu().float().numpy()
+        r = oracle.widen_to_f32(oracle.unpack_dequant(oc, streams[0], n, ORACLE_DT[odt]), ORACLE_DT[odt])
+        same_values(g, r, f"{name} -> {odt}")
+    _, want_sum = oracle.dequant_reduce_requant(oc, streams, n, want_sum=True)
+    _, sums = rca.dequant_reduce_requant([torch.from_numpy(t).to(DEV) for t in streams], c, n, sum_out=True)
+    same_values(sums.cpu().numpy(), want_sum, f"{name} sums")
+
+
 FP8_SCALED = [n for n in VARIANTS if n.startswith(("e4m3_f", "e5m2_f"))]      # FP32 and FP16 scales
 
 
