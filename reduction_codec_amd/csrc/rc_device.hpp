@@ -546,7 +546,9 @@ __device__ __forceinline__ void int4_encode(const float (&v)[32], const EncScale
 
 // acc[e] (+)= q_e * S: the nibbles rebuilt as E4M3 subnormal bytes, decoded
 // times the power-of-two part of `cs` (1 for an FP16 scale, giving q 2^-9,
-// with dm = 512 s; 512 for E8M0, giving q, with dm = 2^e).
+// with dm = 512 s; 512 for E8M0, giving q, with dm = 2^e).  ROUNDED (E8M0
+// exponents whose products can exceed binary32): each product is rounded
+// before it is added.
 template <bool FIRST, int H, bool ROUNDED = false>
 __device__ __forceinline__ void int4_accumulate(const uint32_t (&D)[4], float cs, const float (&dm)[H],
                                                 float (&acc)[32])
@@ -807,6 +809,8 @@ __device__ __forceinline__ void mx_encode(const float (&v)[32], const EncScale (
     }
 }
 
+// acc[e] (+)= code_e * 2^e (dm = 2^e).  ROUNDED: the conversion applies 2^e
+// and rounds, so a product beyond binary32 is +-inf before the add.
 template <bool FIRST, int H, bool ROUNDED = false>
 __device__ __forceinline__ void mx_accumulate(const uint32_t (&D)[4], const float (&dm)[H], float (&acc)[32])
 {
@@ -815,12 +819,17 @@ __device__ __forceinline__ void mx_accumulate(const uint32_t (&D)[4], const floa
         const float p = dm[H == 2 ? d / 2 : 0];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
+            if constexpr (ROUNDED) {                         // the conversion applies 2^e and rounds
+                const f2 v = fp4_dec(D[d], p, b);
+                if (FIRST) { acc[8 * d + 2 * b] = v.x; acc[8 * d + 2 * b + 1] = v.y; }
+                else {
+                    acc[8 * d + 2 * b] = __fadd_rn(acc[8 * d + 2 * b], v.x);
+                    acc[8 * d + 2 * b + 1] = __fadd_rn(acc[8 * d + 2 * b + 1], v.y);
+                }
+                continue;
+            }
             const f2 c = fp4_dec(D[d], 1.0f, b);            // code value, exact
             if (FIRST) { acc[8 * d + 2 * b] = c.x * p; acc[8 * d + 2 * b + 1] = c.y * p; }
-            else if constexpr (ROUNDED) {                    // the product may exceed binary32
-                acc[8 * d + 2 * b] = __fadd_rn(acc[8 * d + 2 * b], __fmul_rn(c.x, p));
-                acc[8 * d + 2 * b + 1] = __fadd_rn(acc[8 * d + 2 * b + 1], __fmul_rn(c.y, p));
-            }
             else {                                            // c * 2^e is exact: one rounding
                 acc[8 * d + 2 * b] = __builtin_fmaf(c.x, p, acc[8 * d + 2 * b]);
                 acc[8 * d + 2 * b + 1] = __builtin_fmaf(c.y, p, acc[8 * d + 2 * b + 1]);

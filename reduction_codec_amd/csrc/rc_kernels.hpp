@@ -27,6 +27,9 @@
 #ifndef RC_REDUCE_WAVES
 #define RC_REDUCE_WAVES 8                          // reduce occupancy target (waves per SIMD), INT / MX
 #endif
+#ifndef RC_MX_REDUCE_WAVES
+#define RC_MX_REDUCE_WAVES 6                       // the same, MXFP4 with 4 or more streams (see ReduceWaves)
+#endif
 #ifndef RC_REDUCE_ROLL
 #define RC_REDUCE_ROLL 1                           // rolling stream loads in the unrolled INT / MX reduce (ReduceRoll)
 #endif
@@ -189,14 +192,16 @@ template <int FMT, int SC> struct SumScale {
 };
 
 // acc (+)= decoded values of the lane's 32 elements (times 2^-P).  ROUNDED,
-// the default with E8M0 scales: every product is rounded before it is added
-// (one multiply and one add instead of an fma), and INT3 codes decode as q
-// with multiplier 2^e.  The same result as the fma while code * 2^e is a
-// binary32 number, and still the definition where it is not: E8M0 bytes from
-// 2^120 (E4M3), 2^113 (E5M2), 2^126 (INT4, E2M1) or 2^127 (INT3, whose
-// usual multiplier 2^(e + 1) would itself be infinite) on.  The encoder never
-// writes those, but any packed bytes can hold them; the fused kernel, which
-// decodes only its own codes, keeps the fma.
+// the default with E8M0 scales: every product is rounded before it is added,
+// and INT3 codes decode as q with multiplier 2^e.  The same result as the fma
+// while code * 2^e is a binary32 number, and still the definition where it is
+// not: E8M0 bytes from 2^120 (E4M3), 2^113 (E5M2), 2^126 (INT4, E2M1) or
+// 2^127 (INT3, whose usual multiplier 2^(e + 1) would itself be infinite) on.
+// The encoder never writes those, but any packed bytes can hold them.  E2M1
+// codes take 2^e as the conversion's scale operand, which rounds the product
+// itself (one add per element, as with the fma); the other formats pay a
+// multiply and an add.  The fused kernel, which decodes only its own codes,
+// keeps the fma.
 template <int FMT, int SC, int BL, bool FIRST, int P = 0, bool ROUNDED = (SC == kSE8)>
 __device__ __forceinline__ void accumulate(const LaneBlock<FMT, SC, BL>& b, float (&acc)[32])
 {
@@ -478,12 +483,18 @@ template <int FMT, int SC, int BL> struct ReduceGroupWaves {
                                  ? 1 : kWavesPerGroup;
 };
 
+// Occupancy target of the reduce (amdgpu_waves_per_eu), which also sets the
+// register budget the compiler schedules for.  INT with E8M0 scales: 7, the
+// rounded decode needs more than 64 registers.  MXFP4 from 4 streams on:
+// with a target of 6 the compiler's schedule fits in 64 registers without
+// spills (so 8 waves still run), with a target of 8 it spills some.
 template <int FMT, int SC, int BL, int K> struct ReduceWaves {
     static constexpr bool kInt = FMT == kInt3 || FMT == kInt4;
     static constexpr bool kVar = BL != 32 || SC == kSE8;
     static constexpr int v = (FMT == kFp8 || FMT == kBf8) ? RC_FP8_REDUCE_WAVES
                            : (kInt && kVar && (K == 0 || K > 4)) ? 6
-                           : (FMT == kInt4 && SC == kSE8) ? 7 : RC_REDUCE_WAVES;
+                           : (kInt && SC == kSE8) ? 7
+                           : (FMT == kMx4 && (K == 0 || K > 3)) ? RC_MX_REDUCE_WAVES : RC_REDUCE_WAVES;
 };
 
 // acc = the K streams' decoded values of the lane's 32 elements of `tile`,
