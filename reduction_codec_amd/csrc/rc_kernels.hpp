@@ -464,12 +464,6 @@ template <int FMT, int SC> struct ReduceRoll {
 template <int FMT> struct ReduceBatch {
     static constexpr int v = (FMT == kFp8 || FMT == kBf8) ? RC_FP8_REDUCE_BATCH : RC_REDUCE_BATCH;
 };
-// Occupancy target of the reduce (waves per SIMD; 8 = at most 64 VGPRs).
-// At 8, the INT kernels with two scales per lane or shared across a lane
-// pair (16- and 64-element blocks) and with E8M0 scales spill registers
-// once more than four streams are unrolled or k is a run-time count; they
-// run at 6 (measured 1.2-1.5x faster at k = 8), INT4 with E8M0 scales at 7
-// below that.  FP8 runs at RC_FP8_REDUCE_WAVES.
 // Waves per workgroup of the reduce.  INT codecs whose tiles are whole
 // 128-byte lines run one-wave workgroups: a freed wave slot is refilled at
 // once, which shortens the ramp and the drain of these ALU-bound kernels
@@ -483,11 +477,16 @@ template <int FMT, int SC, int BL> struct ReduceGroupWaves {
                                  ? 1 : kWavesPerGroup;
 };
 
-// Occupancy target of the reduce (amdgpu_waves_per_eu), which also sets the
-// register budget the compiler schedules for.  INT with E8M0 scales: 7, the
-// rounded decode needs more than 64 registers.  MXFP4 from 4 streams on:
-// with a target of 6 the compiler's schedule fits in 64 registers without
-// spills (so 8 waves still run), with a target of 8 it spills some.
+// Occupancy target of the reduce (amdgpu_waves_per_eu: waves per SIMD, 8 =
+// at most 64 VGPRs), which also sets the register budget the compiler
+// schedules for.  At 8, the INT kernels with two scales per lane or shared
+// across a lane pair (16- and 64-element blocks) and with E8M0 scales spill
+// registers once more than four streams are unrolled or k is a run-time
+// count; they run at 6 (measured 1.2-1.5x faster at k = 8), INT with E8M0
+// scales at 7 below that (their rounded decode needs more than 64
+// registers).  MXFP4 from 4 streams on: with a target of 6 the compiler's
+// schedule fits in 64 registers without spills (so 8 waves still run), with
+// a target of 8 it spills some.  FP8 runs at RC_FP8_REDUCE_WAVES.
 template <int FMT, int SC, int BL, int K> struct ReduceWaves {
     static constexpr bool kInt = FMT == kInt3 || FMT == kInt4;
     static constexpr bool kVar = BL != 32 || SC == kSE8;
