@@ -380,19 +380,36 @@ def decode_codec(c, tile: bytes) -> np.ndarray:
             else:
                 val, neg = table[code & 127], bool(code & 128)
         so = cb + b * SCALE_SIZE[sc]
-        if val is None:
-            r = spec
-        elif sc == 2:
+        if val is None:                                  # NaN / infinite code: IEEE product with the scale
+            if sc == 2:
+                s = np.frombuffer(tile[so:so + 4], dtype=np.float32)[0]
+            elif sc == 1:
+                s = np.float32(np.frombuffer(tile[so:so + 2], dtype=np.float16)[0])
+            else:
+                s = np.float32(np.nan) if tile[so] == 255 else np.float32(2.0 ** (tile[so] - 127))
+            with np.errstate(invalid="ignore"):
+                r = (-spec if neg else spec) * s
+            out[i] = r
+            continue
+        if sc == 2:
             s = np.frombuffer(tile[so:so + 4], dtype=np.float32)[0]
-            r = np.float32(float(val)) * s
+            with np.errstate(all="ignore"):              # non-finite scales: IEEE product
+                r = np.float32(float(val)) * s
         elif sc == 1:
             s = np.frombuffer(tile[so:so + 2], dtype=np.float16)[0]
-            r = np.float32(float(val * Fraction(float(s))))
+            if np.isfinite(s):
+                r = np.float32(float(val * Fraction(float(s))))
+                if r == 0 and np.signbit(s):                 # a zero product takes the scale's sign too
+                    r = np.float32(-0.0)
+            else:                                        # +-inf or NaN scale: IEEE product
+                with np.errstate(invalid="ignore"):
+                    r = np.float32(float(val)) * np.float32(s)
         else:
             if tile[so] == 255:
                 r = np.float32(np.nan)
-            else:
-                r = np.float32(float(val * Fraction(2) ** (tile[so] - 127)))
+            else:                                        # rounded once: +-inf beyond binary32
+                with np.errstate(over="ignore"):
+                    r = np.float32(float(val * Fraction(2) ** (tile[so] - 127)))
         out[i] = -r if neg else r
     return out
 

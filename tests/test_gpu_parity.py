@@ -14,7 +14,8 @@ import torch
 import datagen
 import oracle
 import reduction_codec_amd as rca
-from tests import fp8_ties
+from tests import brute, fp8_ties
+from tests.test_oracle_variants import SPECIAL_SCALES
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -531,15 +532,19 @@ def same_values(got: np.ndarray, ref: np.ndarray, what: str):
 def test_decode_of_arbitrary_bytes(name):
     """Decoding is defined for every bit pattern of codes and scales (NaN,
     infinite, negative and subnormal scales, FP8 NaN / infinity codes, the
-    E8M0 NaN byte): packed streams of random bytes unpack to fp32, bf16 and
-    fp16, and two of them reduce to the FP32 sums, as the oracle decodes them
-    (a NaN matching any NaN).  The requantized codes of non-finite sums are
-    unspecified and not compared."""
+    E8M0 NaN byte and the E8M0 exponents whose products overflow binary32,
+    planted in the first tile): packed streams of random bytes unpack to
+    fp32, bf16 and fp16, and two of them reduce to the FP32 sums, as the
+    oracle decodes them (a NaN matching any NaN).  The requantized codes of
+    non-finite sums are unspecified and not compared."""
     n = 16 * 2048 + 100
     say(f"case decode of arbitrary bytes {name}")
     oc, c = oracle.ALL_CODECS[name], rca.ALL_CODECS[name]
     rng = np.random.default_rng(len(name) * 131)
     streams = [rng.integers(0, 256, oracle.packed_bytes(oc, n), dtype=np.uint8) for _ in range(2)]
+    sp, at = SPECIAL_SCALES[oc[1]], brute.CODE_BYTES[oc[0]]
+    streams[0][at:at + sp.size] = sp                  # the scale extremes in tile 0 of both streams,
+    streams[1][at:at + sp.size] = sp.reshape(-1, brute.SCALE_SIZE[oc[1]])[::-1].reshape(-1)  # other pairings
     d0 = torch.from_numpy(streams[0]).to(DEV)
     same_values(rca.unpack_dequant(d0, c, n, torch.float32).cpu().numpy(),
                 oracle.unpack_dequant(oc, streams[0], n, oracle.DT_FP32), f"{name} -> fp32")

@@ -248,3 +248,51 @@ def test_fp16_scaled_fp8_zero_and_subnormal_scales():
     p = oracle.quantize_pack(c, v)
     assert not p[:16].any() and not p[1024:1040].any() and not p[2048:2050].any()
     assert p.tobytes() == brute.encode_codec(c, v)
+
+
+# ---- decode of arbitrary bytes ------------------------------------------------
+
+SPECIAL_SCALES = {
+    1: np.array([0x7C00, 0xFC00, 0x7E00, 0xFE00, 0x0001, 0x8001, 0x8000, 0x0000, 0x7BFF, 0xFBFF],
+                dtype=np.uint16).view(np.uint8),
+    2: np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0x00000001, 0x80000000, 0x7F7FFFFF, 0xFF7FFFFF,
+                 0x00800000], dtype=np.uint32).view(np.uint8),
+    3: np.array([0, 1, 126, 127, 128, 239, 240, 246, 247, 252, 253, 254, 255], dtype=np.uint8),
+}
+
+
+def arbitrary_tile(c, seed: int) -> np.ndarray:
+    """One tile of random bytes for codec c, its first block scales set to
+    the extremes of the scale type: infinite, NaN, subnormal and largest
+    FP16/FP32 scales, and for E8M0 the bytes around each format's overflow
+    threshold, 2^127 and NaN."""
+    fmt, sc, _ = c
+    b = np.random.default_rng(seed).integers(0, 256, brute.codec_tile_bytes(c), dtype=np.uint8)
+    sp = SPECIAL_SCALES[sc]
+    b[brute.CODE_BYTES[fmt]:brute.CODE_BYTES[fmt] + sp.size] = sp
+    return b
+
+
+def same_values(got, ref):
+    g, r = np.asarray(got, dtype=np.float32), np.asarray(ref, dtype=np.float32)
+    ok = (g.view(np.uint32) == r.view(np.uint32)) | (np.isnan(g) & np.isnan(r))
+    assert ok.all(), [(int(i), float(g[i]), float(r[i])) for i in np.nonzero(~ok)[0][:6]]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_decode_of_arbitrary_bytes_equals_brute_decode(name):
+    """Every bit pattern decodes to fp32(code * scale), rounded once (the
+    brute-force decode in exact rationals; IEEE products for non-finite
+    scales): NaN and infinite codes and scales, subnormal scales, and E8M0
+    exponents whose products overflow binary32.  Two such streams reduce to
+    the binary32 sums of those values."""
+    c = oracle.ALL_CODECS[name]
+    t0, t1 = arbitrary_tile(c, 11), arbitrary_tile(c, 12)
+    d0, d1 = brute.decode_codec(c, t0.tobytes()), brute.decode_codec(c, t1.tobytes())
+    same_values(oracle.unpack_dequant(c, t0, 2048, oracle.DT_FP32), d0)
+    _, sums = oracle.dequant_reduce_requant(c, [t0, t1], 2048, want_sum=True)
+    with np.errstate(all="ignore"):
+        want = (d0 + d1).astype(np.float32)
+    same_values(sums, want)
+    if c[1] == 3:                                   # the planted E8M0 bytes reach binary32's end
+        assert np.isinf(d0).any() and np.isnan(d0).any()
