@@ -330,22 +330,26 @@ def encode_codec(c, x_f32: np.ndarray) -> bytes:
                 else:
                     table = E4M3 if fmt == 3 else E5M2
                     codes[i] = (sign << 7) | nearest_code(Fraction(abs(float(vb[e]))) / den, table)
-        if fmt in (1, 4):
-            body = _nibbles_to_bytes(codes)
-        elif fmt == 2:
-            q2w, q1w = [], []
-            for g in range(64):
-                nib = codes[32 * g:32 * g + 32]
-                N = [sum(nib[4 * j + k] << (4 * j) for j in range(8)) for k in range(4)]
-                m = 0x33333333
-                q2w += [(N[0] & m) | ((N[1] & m) << 2), (N[2] & m) | ((N[3] & m) << 2)]
-                q1w.append(((N[0] >> 3) & 0x11111111) | ((N[1] >> 2) & 0x22222222) |
-                           ((N[2] >> 1) & 0x44444444) | (N[3] & 0x88888888))
-            body = _words_to_bytes(q2w) + _words_to_bytes(q1w)
-        else:
-            body = fp8_planes(codes)
-        out += body + bytes(scales)
+        out += code_region(fmt, codes) + bytes(scales)
     return out
+
+
+def code_region(fmt: int, codes) -> bytes:
+    """The code bytes of one tile from its 2048 sign-magnitude codes in
+    element order (INT3: sign << 3 | magnitude)."""
+    if fmt in (1, 4):
+        return _nibbles_to_bytes(codes)
+    if fmt == 2:
+        q2w, q1w = [], []
+        for g in range(64):
+            nib = codes[32 * g:32 * g + 32]
+            N = [sum(nib[4 * j + k] << (4 * j) for j in range(8)) for k in range(4)]
+            m = 0x33333333
+            q2w += [(N[0] & m) | ((N[1] & m) << 2), (N[2] & m) | ((N[3] & m) << 2)]
+            q1w.append(((N[0] >> 3) & 0x11111111) | ((N[1] >> 2) & 0x22222222) |
+                       ((N[2] >> 1) & 0x44444444) | (N[3] & 0x88888888))
+        return _words_to_bytes(q2w) + _words_to_bytes(q1w)
+    return fp8_planes(codes)
 
 
 def decode_codec(c, tile: bytes) -> np.ndarray:

@@ -15,7 +15,7 @@ import datagen
 import oracle
 import reduction_codec_amd as rca
 from tests import brute, fp8_ties
-from tests.test_oracle_variants import SPECIAL_SCALES
+from tests.test_oracle_variants import CODE_BITS, E8M0_CODECS, SPECIAL_SCALES, e8m0_every_pair_stream
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -555,6 +555,28 @@ def test_decode_of_arbitrary_bytes(name):
     _, want_sum = oracle.dequant_reduce_requant(oc, streams, n, want_sum=True)
     _, sums = rca.dequant_reduce_requant([torch.from_numpy(t).to(DEV) for t in streams], c, n, sum_out=True)
     same_values(sums.cpu().numpy(), want_sum, f"{name} sums")
+
+
+@pytest.mark.parametrize("name", E8M0_CODECS)
+def test_e8m0_every_code_with_every_scale_byte(name):
+    """Every code pattern under every E8M0 scale byte, products beyond
+    binary32 and the NaN byte included: unpack to fp32, bf16 and fp16 and the
+    FP32 sums of two such streams (the codes paired differently) equal the
+    oracle's (a NaN matching any NaN)."""
+    oc, c = oracle.ALL_CODECS[name], rca.ALL_CODECS[name]
+    a, n = e8m0_every_pair_stream(oc)
+    b, _ = e8m0_every_pair_stream(oc, rot=(1 << CODE_BITS[oc[0]]) // 2 + 1)
+    say(f"case e8m0 every pair {name} n={n}")
+    da = torch.from_numpy(a).to(DEV)
+    same_values(rca.unpack_dequant(da, c, n, torch.float32).cpu().numpy(),
+                oracle.unpack_dequant(oc, a, n, oracle.DT_FP32), f"{name} -> fp32")
+    for odt, tdt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        g = rca.unpack_dequant(da, c, n, tdt).cpu().float().numpy()
+        r = oracle.widen_to_f32(oracle.unpack_dequant(oc, a, n, ORACLE_DT[odt]), ORACLE_DT[odt])
+        same_values(g, r, f"{name} -> {odt}")
+    _, want = oracle.dequant_reduce_requant(oc, [a, b], n, want_sum=True)
+    _, sums = rca.dequant_reduce_requant([da, torch.from_numpy(b).to(DEV)], c, n, sum_out=True)
+    same_values(sums.cpu().numpy(), want, f"{name} sums")
 
 
 FP8_SCALED = [n for n in VARIANTS if n.startswith(("e4m3_f", "e5m2_f"))]      # FP32 and FP16 scales

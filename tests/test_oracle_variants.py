@@ -296,3 +296,64 @@ def test_decode_of_arbitrary_bytes_equals_brute_decode(name):
     same_values(sums, want)
     if c[1] == 3:                                   # the planted E8M0 bytes reach binary32's end
         assert np.isinf(d0).any() and np.isnan(d0).any()
+
+
+CODE_BITS = {1: 4, 2: 3, 3: 8, 4: 4, 5: 8}          # INT4, INT3, E4M3, E2M1, E5M2
+E8M0_CODECS = [n for n in ALL if oracle.ALL_CODECS[n][1] == 3]
+
+
+def e8m0_every_pair_stream(c, rot: int = 0):
+    """Packed tiles of an E8M0 codec in which every code pattern meets every
+    scale byte: block B has scale byte B mod 256, and its element e the code
+    (block * (B div 256) + e + rot) mod 2^width, so the blocks sharing a
+    scale byte run through all codes.  Returns (bytes, element count)."""
+    fmt, _, bl = c
+    ncode = 1 << CODE_BITS[fmt]
+    reps = max(1, ncode // bl)
+    per_tile = brute.TILE // bl
+    tiles = 256 * reps // per_tile
+    out = bytearray()
+    for t in range(tiles):
+        codes, scales = [], bytearray()
+        for b in range(per_tile):
+            blk = t * per_tile + b
+            scales.append(blk % 256)
+            for e in range(bl):
+                code = (bl * (blk // 256) + e + rot) % ncode
+                codes.append(((code >> 2) << 3) | (code & 3) if fmt == 2 else code)
+        out += brute.code_region(fmt, codes) + bytes(scales)
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy(), tiles * brute.TILE
+
+
+@pytest.mark.parametrize("name", E8M0_CODECS)
+def test_e8m0_every_pair_stream_covers_every_pair(name):
+    """The stream really pairs every code with every scale byte (read back
+    with the brute-force layout), and the oracle decodes it as brute force
+    does, overflowing products included."""
+    c = oracle.ALL_CODECS[name]
+    fmt, _, bl = c
+    p, n = e8m0_every_pair_stream(c)
+    tb = brute.codec_tile_bytes(c)
+    seen = set()
+    for t in range(n // brute.TILE):
+        tile = p[t * tb:(t + 1) * tb].tobytes()
+        for i in range(brute.TILE):
+            sb = tile[brute.CODE_BYTES[fmt] + i // bl]
+            if fmt in (1, 4):
+                code = (tile[i // 2] >> (4 * (i % 2))) & 15
+            elif fmt == 2:
+                code = None                          # checked through the decode below
+            else:
+                code = brute.fp8_byte(tile, i)
+            seen.add((code, sb))
+        if t < 2:
+            same_values(oracle.unpack_dequant(c, p[t * tb:(t + 1) * tb], brute.TILE, oracle.DT_FP32),
+                        brute.decode_codec(c, tile))
+    if fmt != 2:
+        assert len(seen) == (1 << CODE_BITS[fmt]) * 256
+    else:
+        d = oracle.unpack_dequant(c, p, n, oracle.DT_FP32).reshape(-1, bl)
+        sbytes = np.concatenate([p[t * tb + brute.CODE_BYTES[fmt]:(t + 1) * tb] for t in range(n // brute.TILE)])
+        for s in (1, 127, 200):                      # exponents where every product is finite
+            vals = set(np.unique(d[sbytes == s]).tolist())
+            assert vals == {float(np.float32(q * 2.0 ** (s - 127))) for q in range(-3, 4)}
