@@ -506,8 +506,9 @@ def fused_table(args):
         for K in [int(v) for v in args.table_k.split(",")]:
             msgs = [torch.from_numpy(datagen.bf16_student4(2 * n, 500 + j).view(np.int16)).view(torch.bfloat16).to(dev)
                     for j in range(K)]
-            for fmt in ("int3", "int4", "fp8", "mxfp4"):
-                c = rca.CODECS[fmt]
+            names = sorted(rca.ALL_CODECS) if args.table_codecs == "all" else args.table_codecs.split(",")
+            for fmt in names:
+                c = rca.CODECS[fmt] if fmt in rca.CODECS else rca.ALL_CODECS[fmt]
                 pb = rca.packed_bytes(c, n)
                 out = torch.empty(n, dtype=torch.bfloat16, device=dev)
                 packed = torch.empty(pb, dtype=torch.uint8, device=dev)

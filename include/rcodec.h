@@ -175,9 +175,8 @@ rc_status rc_dequant_reduce_requant(rc_codec c, const void *const *ins, int k, s
  * rc_dequant_reduce_requant with sums, rc_unpack_dequant), in one kernel
  * pass that touches only the messages, out and packed_out.
  *   msgs: host array of k device pointers to n elements of dt each;
- *   out:  n elements of dt.  Default codecs only ({INT4, FP16, 32},
- *   {INT3, FP16, 32}, {FP8_E4M3, FP32, 32}, {MXFP4, E8M0, 32}); others
- *   return RC_ERR_UNSUPPORTED.  Errors as for rc_dequant_reduce_requant. */
+ *   out:  n elements of dt.  Every supported codec.  Errors as for
+ *   rc_dequant_reduce_requant. */
 rc_status rc_allreduce_emulate(rc_codec c, rc_dtype dt, const void *const *msgs, int k, size_t n,
                                int two_shot, void *out, void *packed_out, void *stream);
 

@@ -95,12 +95,7 @@ rc_status rc_dequant_reduce_requant(rc_codec c, const void* const* ins, int k, s
 rc_status rc_allreduce_emulate(rc_codec c, rc_dtype dt, const void* const* msgs, int k, size_t n, int two_shot,
                                void* out, void* packed_out, void* stream)
 {
-    if (!codec_ok(c) || !dtype_ok(dt) || c.block != RC_BLOCK_ELEMS) return RC_ERR_UNSUPPORTED;
-    const bool dflt = (c.format == RC_FMT_INT4 && c.scale == RC_SCALE_FP16) ||
-                      (c.format == RC_FMT_INT3 && c.scale == RC_SCALE_FP16) ||
-                      (c.format == RC_FMT_FP8_E4M3 && c.scale == RC_SCALE_FP32) ||
-                      (c.format == RC_FMT_MXFP4 && c.scale == RC_SCALE_E8M0);
-    if (!dflt) return RC_ERR_UNSUPPORTED;
+    if (!codec_ok(c) || !dtype_ok(dt)) return RC_ERR_UNSUPPORTED;
     if (k < 1 || k > RC_MAX_STREAMS) return RC_ERR_RANGE;
     if (n == 0) return RC_OK;
     if (n > kMaxElems) return RC_ERR_RANGE;

@@ -11,15 +11,18 @@ enum : int { S16 = 1, S32 = 2, SE8 = 3 };
 typedef hipError_t (*QuantizeFn)(int, const void*, size_t, void*, hipStream_t);
 typedef hipError_t (*UnpackFn)(const void*, size_t, int, void*, hipStream_t);
 typedef hipError_t (*ReduceFn)(const StreamPtrs&, int, size_t, void*, float*, hipStream_t);
+typedef hipError_t (*AllreduceFn)(int, const StreamPtrs&, int, size_t, int, void*, void*, hipStream_t);
 
 struct Entry {
     int fmt, sc, bl;
     QuantizeFn q;
     UnpackFn u;
     ReduceFn r;
+    AllreduceFn a;
 };
 
-#define RC_ENTRY(F, S, B, R) {F, S, B, &launch_quantize_t<F, S, B>, &launch_unpack_t<F, S, B>, &R<F, S, B>}
+#define RC_ENTRY(F, S, B, R)                                                                  \
+    {F, S, B, &launch_quantize_t<F, S, B>, &launch_unpack_t<F, S, B>, &R<F, S, B>, &launch_allreduce_t<F, S, B>}
 
 const Entry kCodecs[] = {
     RC_ENTRY(kInt4, S16, 32, launch_reduce_unrolled_t),
@@ -85,16 +88,11 @@ hipError_t launch_reduce(int fmt, int sc, int bl, const StreamPtrs& p, int k, si
     return e ? e->r(p, k, n, out, sum, st) : hipErrorInvalidValue;
 }
 
-// The fused all-reduce emulation exists for the four default codecs.
 hipError_t launch_allreduce(int fmt, int sc, int bl, int dtype, const StreamPtrs& msgs, int k, size_t n, int two_shot,
                             void* out, void* packed, hipStream_t st)
 {
-    if (bl != 32) return hipErrorInvalidValue;
-    if (fmt == kInt4 && sc == S16) return launch_allreduce_t<kInt4, S16, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
-    if (fmt == kInt3 && sc == S16) return launch_allreduce_t<kInt3, S16, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
-    if (fmt == kFp8 && sc == S32) return launch_allreduce_t<kFp8, S32, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
-    if (fmt == kMx4 && sc == SE8) return launch_allreduce_t<kMx4, SE8, 32>(dtype, msgs, k, n, two_shot, out, packed, st);
-    return hipErrorInvalidValue;
+    const Entry* e = find(fmt, sc, bl);
+    return e ? e->a(dtype, msgs, k, n, two_shot, out, packed, st) : hipErrorInvalidValue;
 }
 
 }  // namespace rc

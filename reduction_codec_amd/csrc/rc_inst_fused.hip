@@ -1,4 +1,5 @@
-// Fused all-reduce emulation kernels of the four default codecs.
+// Fused all-reduce emulation kernels of the four default codecs (the variant
+// codecs' are in rc_inst_fused_int/e4m3/e5m2.hip).
 #include "rc_inst.hpp"
 
 using namespace rc;

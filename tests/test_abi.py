@@ -169,8 +169,10 @@ def test_allreduce_emulate_error_paths():
         arr = None if ptrs is None else (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
         return l.rc_allreduce_emulate(codec, dt, arr, k, n, two_shot, out, packed, None)
 
-    assert ar(rca.ALL_CODECS["int3_e8m0_b32"], 3, [A], 1, 10, A) == rca.ERR_UNSUPPORTED   # default codecs only
-    assert ar(rca.ALL_CODECS["int3_f16_b16"], 3, [A], 1, 10, A) == rca.ERR_UNSUPPORTED
+    assert ar(rca.Codec(2, 2, 32), 3, [A], 1, 10, A) == rca.ERR_UNSUPPORTED       # INT3 with an FP32 scale
+    assert ar(rca.Codec(3, 2, 48), 3, [A], 1, 10, A) == rca.ERR_UNSUPPORTED       # block of 48
+    for name in rca.ALL_CODECS:                                                    # every codec: n = 0 is a no-op
+        assert ar(rca.ALL_CODECS[name], 3, [A], 1, 0, A) == rca.OK, name
     assert ar(rca.INT3, 9, [A], 1, 10, A) == rca.ERR_UNSUPPORTED
     assert ar(rca.INT3, 3, [A], 0, 10, A) == rca.ERR_RANGE
     assert ar(rca.INT3, 3, [A] * 17, 17, 10, A) == rca.ERR_RANGE

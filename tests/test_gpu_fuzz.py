@@ -89,7 +89,7 @@ def test_fuzz_quantize_reduce_unpack(name, dt, n, k, seed, kinds):
     assert ((y.view(np.uint32) == ref_y.view(np.uint32)) | (np.isnan(y) & np.isnan(ref_y))).all(), "unpack"
 
 
-FUSED = ["int4", "int3", "fp8", "mxfp4"]
+FUSED = CODECS
 
 
 @settings(max_examples=max(1, EXAMPLES // 2), deadline=None, derandomize=EXAMPLES == 120, database=None,
@@ -106,8 +106,8 @@ def test_fuzz_allreduce_emulate(fmt, dt, n, k, two_shot, seed, kinds):
           flush=True)
     rng = np.random.default_rng(seed)
     xs = [make_values(rng, n, kinds[j % len(kinds):] + kinds[:j % len(kinds)], k, dt) for j in range(k)]
-    ref, ref_packed = oracle.allreduce_emulate(oracle.CODECS[fmt], xs, DTYPES[dt][1], two_shot=two_shot)
-    out, packed = rca.allreduce_emulate([to_dev(x, dt) for x in xs], rca.CODECS[fmt], two_shot=two_shot,
+    ref, ref_packed = oracle.allreduce_emulate(oracle.ALL_CODECS[fmt], xs, DTYPES[dt][1], two_shot=two_shot)
+    out, packed = rca.allreduce_emulate([to_dev(x, dt) for x in xs], rca.ALL_CODECS[fmt], two_shot=two_shot,
                                         packed_out=two_shot)
     g = out.cpu()
     g = g.numpy() if dt == "fp32" else g.view(torch.int16).numpy().view(np.uint16)

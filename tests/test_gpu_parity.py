@@ -677,6 +677,27 @@ def test_allreduce_emulate_bit_exact(fmt, dt, two_shot, k):
         assert_same(host_u8(packed), ref_packed, "packed sum")
 
 
+@pytest.mark.parametrize("name", VARIANTS)
+@pytest.mark.parametrize("two_shot", [True, False])
+def test_allreduce_emulate_variants_bit_exact(name, two_shot):
+    """The fused emulation for every codec (the message dtype and the
+    message count vary with the codec): output and requantized sum equal the
+    oracle's composition of quantize, reduce and unpack."""
+    i = VARIANTS.index(name)
+    dt, k = sorted(DTYPES)[i % 3], 2 + i % 3
+    n = 2 * 2048 + 700
+    say(f"case allreduce variant {name} dt={dt} two_shot={two_shot} k={k}")
+    msgs = [mixed(n, seed=700 + 13 * i + j, dt=dt) for j in range(k)]
+    ref, ref_packed = oracle.allreduce_emulate(oracle.ALL_CODECS[name], msgs, ORACLE_DT[dt], two_shot=two_shot)
+    out, packed = rca.allreduce_emulate([to_dev(m, dt) for m in msgs], rca.ALL_CODECS[name], two_shot=two_shot,
+                                        packed_out=two_shot)
+    g = out.cpu()
+    g = g.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else g.numpy()
+    assert_same(g, ref, f"allreduce {name} {dt}")
+    if two_shot:
+        assert_same(host_u8(packed), ref_packed, "packed sum")
+
+
 @pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("two_shot", [True, False])
 @pytest.mark.parametrize("k", [1, 2, 3])
