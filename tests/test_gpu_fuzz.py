@@ -6,8 +6,10 @@ Hypothesis draws the codec (any of the 33), the input dtype, the length
 is an fp16 subnormal or flushes to zero, fp32 denormals, saturating and huge
 blocks, outliers); every example quantizes K streams, reduces them with the
 FP32 sums and unpacks the result, each step compared byte for byte with the
-oracle.  By default the 120-example sequence is derandomized, so a run is
-reproducible; RC_FUZZ_EXAMPLES=N runs N examples with fresh random draws.
+oracle.  Further tests fuzz the fused all-reduce emulation, the decode of
+streams of random bytes and the MXFP4 GEMV.  By default the 120-example
+sequence is derandomized, so a run is reproducible; RC_FUZZ_EXAMPLES=N runs N
+examples with fresh random draws (N/2 for the emulation, N/3 for the others).
 """
 import os
 
@@ -119,6 +121,28 @@ def test_fuzz_allreduce_emulate(fmt, dt, n, k, two_shot, seed, kinds):
         assert np.array_equal(g, r), "output"
     if two_shot:
         assert np.array_equal(packed.cpu().numpy(), ref_packed), "packed sum"
+
+
+@settings(max_examples=max(1, EXAMPLES // 3), deadline=None, derandomize=EXAMPLES == 120, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(name=st.sampled_from(CODECS), n=st.integers(min_value=1, max_value=4 * 2048 + 200),
+       k=st.integers(min_value=1, max_value=5), seed=st.integers(min_value=0, max_value=2**31 - 1))
+def test_fuzz_decode_of_random_bytes(name, n, k, seed):
+    """Packed streams of random bytes (any code, any scale bits): unpack to
+    fp32 and the FP32 sums of k of them equal the oracle's, a NaN matching
+    any NaN; the requantized codes of non-finite sums are unspecified."""
+    print(f"case fuzz random bytes {name} n={n} k={k} seed={seed}", flush=True)
+    rng = np.random.default_rng(seed)
+    c_or, c = oracle.ALL_CODECS[name], rca.ALL_CODECS[name]
+    streams = [rng.integers(0, 256, oracle.packed_bytes(c_or, n), dtype=np.uint8) for _ in range(k)]
+    dev = [torch.from_numpy(t).to(DEV) for t in streams]
+    y, ref_y = rca.unpack_dequant(dev[0], c, n, torch.float32).cpu().numpy(), \
+        oracle.unpack_dequant(c_or, streams[0], n, oracle.DT_FP32)
+    assert ((y.view(np.uint32) == ref_y.view(np.uint32)) | (np.isnan(y) & np.isnan(ref_y))).all(), "unpack"
+    _, ref_sums = oracle.dequant_reduce_requant(c_or, streams, n, want_sum=True)
+    _, sums = rca.dequant_reduce_requant(dev, c, n, sum_out=True)
+    s = sums.cpu().numpy()
+    assert ((s.view(np.uint32) == ref_sums.view(np.uint32)) | (np.isnan(s) & np.isnan(ref_sums))).all(), "sums"
 
 
 @settings(max_examples=max(1, EXAMPLES // 3), deadline=None, derandomize=EXAMPLES == 120, database=None,
