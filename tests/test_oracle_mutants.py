@@ -46,6 +46,12 @@ MUTANTS = {
     "fp8_single_plane_order": ("return e < 16 ? 16 * g + e : 1024 + 16 * g + (e - 16);", "return i;"),
     "int3_pair_order_swapped": ("4 * (p / 2) + 2 * (e % 2);", "4 * (p / 2) + 2 * (1 - e % 2);"),
     "minifloat_ties_away_from_zero": ("return (c % 2 == 0) ? c : c + 1;", "return c + 1;"),
+    "e8m0_decode_saturates": ("return (float)ldexp(val, (int)sp[0] - 127);",
+                              "return (float)fmax(-3.4028234663852886e38, "
+                              "fmin(3.4028234663852886e38, ldexp(val, (int)sp[0] - 127)));"),
+    "e8m0_nan_byte_read_as_exponent": ("if (sp[0] == 0xFF) return NAN;", "if (sp[0] == 0x100) return NAN;"),
+    "fp16_scale_sign_dropped": ("return (float)(val * rco_f16_to_f32(get_u16(sp)));",
+                                "return (float)(val * fabs(rco_f16_to_f32(get_u16(sp))));"),
     "fp8_quotient_rounded_to_binary32_first": (
         "(unsigned)mag_of(fabs((double)vb[e]), den));",
         "(unsigned)mag_of((double)(float)(fabs((double)vb[e]) / den), 1.0));"),
