@@ -15,7 +15,7 @@ import datagen
 import oracle
 import reduction_codec_amd as rca
 from tests import brute, fp8_ties
-from tests.test_oracle_variants import CODE_BITS, E8M0_CODECS, SPECIAL_SCALES, e8m0_every_pair_stream
+from tests.arbitrary import CODE_BITS, E8M0_CODECS, SPECIAL_SCALES, e8m0_every_pair_stream
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
