@@ -140,8 +140,9 @@ rc_status rc_quantize_pack(rc_codec c, rc_dtype in_t, const void *in, size_t n,
 
 /* Decode n elements of the packed stream `in` (rc_packed_bytes(c, n) bytes)
  * to dtype out_t at `out` (n * sizeof(out_t) bytes): each value is code times
- * block scale computed in FP32 (exact for INT/FP16 and E2M1/E8M0, one binary32
- * product for FP8 with an FP32 scale), then written as fp32, or rounded to
+ * block scale computed in FP32 (exact with FP16 and E8M0 scales while the
+ * product is a binary32 number, one binary32 product for FP8 with an FP32
+ * scale; "Decode of any bytes" above), then written as fp32, or rounded to
  * bf16 / fp16 (nearest even, fp16 overflow to +-inf).  This is the receiving
  * side's decode: payloads travel compressed and the arithmetic on them stays
  * in FP32 (RCCLX -- Low-Precision Collectives; QuickReduce INT3 page --
