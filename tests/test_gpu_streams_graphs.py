@@ -6,8 +6,9 @@ tests check both against the CPU oracle: work launched on a non-default
 stream, and a captured quantize -> 4-stream reduce -> unpack pipeline
 replayed several times with new inputs written eagerly between the replays
 (each replay must compute from the inputs it finds, and no replay may reuse
-an earlier result); and the two in-place uses the header allows (the reduce
-into its first stream, the all-reduce emulation into one of its messages).
+an earlier result); the two in-place uses the header allows (the reduce
+into its first stream, the all-reduce emulation into one of its messages);
+and host threads calling the library at once, each on its own stream.
 """
 import numpy as np
 import pytest
@@ -158,3 +159,54 @@ def test_stream_argument_without_switching_streams(fmt):
     assert np.array_equal(p0.cpu().numpy(), ref_p0)
     assert np.array_equal(out.cpu().numpy(), ref_out)
     assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref_y)
+
+
+def test_host_threads_on_their_own_streams():
+    """The library keeps no state, so host threads may call it at once: four
+    threads, each on its own stream with its own codec and data, run the
+    quantize -> 4-stream reduce -> unpack pipeline ten times over; every
+    result equals the oracle's."""
+    import threading
+
+    print("case host threads", flush=True)
+    refs, work = {}, {}
+    for t, fmt in enumerate(FMTS):
+        x = message(40 + t)
+        peers = [oracle.quantize_pack(oracle.CODECS[fmt], message(50 + 4 * t + j), dtype=oracle.DT_BF16)
+                 for j in range(3)]
+        refs[fmt] = oracle_pipeline(fmt, x, peers)
+        work[fmt] = (bf16_dev(x), [torch.from_numpy(p).to(DEV) for p in peers])
+    rca.lib()                                      # loaded once, before the threads
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def run(fmt):
+        try:
+            side = torch.cuda.Stream(device=DEV)
+            xd, pd = work[fmt]
+            c = rca.CODECS[fmt]
+            with torch.cuda.stream(side):
+                got = []
+                for _ in range(10):
+                    p0 = rca.quantize_pack(xd, c, stream=side)
+                    out, _ = rca.dequant_reduce_requant([p0] + pd, c, N, stream=side)
+                    y = rca.unpack_dequant(out, c, N, torch.bfloat16, stream=side)
+                    got.append((p0, out, y))
+            side.synchronize()
+            results[fmt] = got
+        except Exception as e:                     # reported by the main thread
+            errors.append((fmt, repr(e)))
+
+    threads = [threading.Thread(target=run, args=(fmt,)) for fmt in FMTS]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not errors, errors
+    assert all(not th.is_alive() for th in threads)
+    for fmt in FMTS:
+        ref_p0, ref_out, ref_y = refs[fmt]
+        for p0, out, y in results[fmt]:
+            assert np.array_equal(p0.cpu().numpy(), ref_p0), fmt
+            assert np.array_equal(out.cpu().numpy(), ref_out), fmt
+            assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref_y), fmt
