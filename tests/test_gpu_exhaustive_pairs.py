@@ -9,7 +9,9 @@ Formats for Deep Learning" (abstract) under the block scales of "RCCLX:
 Innovating GPU communications on AMD platforms" (Low-Precision Collectives)
 -- and so must the INT3 / INT4 codes with FP16 block scales (round half to
 even of the exact quotient, "QuickReduce INT3 Quantization and Benchmarking
-on MI355", Method).  The bf16 pairs also run as fp32 input, which takes the
+on MI355", Method), and every element format under E8M0 block scales
+("Microscaling Data Formats for Deep Learning", abstract: the nearest code
+of the value times a power of two).  The bf16 pairs also run as fp32 input, which takes the
 FP8 encoder's exact fallback wherever a quotient sits on a rounding
 midpoint.  This checks on the hardware what tests/device_arith.c checks by
 emulation.
@@ -27,7 +29,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 TOP = {"bf16": 0x7F7F, "fp16": 0x7BFF}           # largest finite positive bit pattern
 CHUNK_BLOCKS = 1 << 20                             # 32 Mi elements per launch
-# every block maximum (all 18 cases: about 50 s on an MI355X machine);
+# every block maximum (all 33 cases: about 90 s on an MI355X machine);
 # RC_FP8_PAIR_STEP=17 takes every 17th, with every x below it, for a quick run
 A_STEP = int(os.environ.get("RC_FP8_PAIR_STEP", "1"))
 
@@ -54,7 +56,8 @@ def pair_blocks(dt: str):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["e4m3_f32_b32", "e4m3_f16_b32", "e5m2_f32_b32", "e5m2_f16_b32",
-                                  "int3_f16_b32", "int4_f16_b32"])
+                                  "int3_f16_b32", "int4_f16_b32", "e4m3_e8m0_b32", "e5m2_e8m0_b32",
+                                  "int3_e8m0_b32", "int4_e8m0_b32", "e2m1_e8m0_b32"])
 @pytest.mark.parametrize("src,dt", [("bf16", "bf16"), ("fp16", "fp16"), ("bf16", "fp32")])
 def test_every_narrow_pair(name, src, dt):
     c, oc = rca.ALL_CODECS[name], oracle.ALL_CODECS[name]
