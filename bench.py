@@ -17,8 +17,13 @@ events around a graph of back-to-back launches, against 8 TB/s) and a
 the same workload).
 
 Extra modes:
-  --table                               per-kernel table over all formats and
-                                        sizes (--table-mib)
+  --table                               per-kernel table over codecs (--table-codecs),
+                                        sizes (--table-mib), stream counts
+                                        (--table-k) and message dtypes (--table-dt)
+  --fused                               the one-kernel all-reduce emulation against
+                                        the separate kernels
+  --gemv                                the MXFP4 GEMV on the 4096 x 4096 weight recipe
+  --summarize-trace RESULTS_DB          kernel-duration table of a rocprofv3 trace
   --summarize-pmc FETCH_DIR WRITE_DIR [SQ_DIR]
                                         turn `rocprofv3 --pmc` runs of this
                                         script into profiles/traffic_*.json
