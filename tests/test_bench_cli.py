@@ -88,3 +88,16 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() != h0                      # code
     src.write_text('// header\nint f(int x) { return x + 1; }  /* note */\nconst char* s = "a /// b";\n')
     assert bench.kernel_source_hash() != h0                      # a string literal is code
+
+
+def test_committed_counters_are_for_these_kernels():
+    """The stored HBM traffic and VALU counts were taken on the kernel code of
+    this tree (bench.py drops them from its JSON line otherwise), and they say
+    that the dominant kernels move what the method must move and no more."""
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    assert t["kernel_source_sha"] == bench.kernel_source_hash()
+    for name, alg in (("reduce_kernel", 73400320), ("quantize_kernel", 81788928)):
+        k = t["kernels"][name]
+        assert 1.0 <= k["bytes"] / alg < 1.01, name
+        assert k["valu_insts"] > 0, name
